@@ -1,0 +1,164 @@
+/*
+ * ul.h - C ABI of the per-rank hot path of Ulysses sequence parallelism on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * The path has three steps (page "Hugging Face并行加速：10倍提升超长序列训练效率",
+ * nmedialink.com, section "Ulysses的工作原理", steps 1-5; page "DeepSpeed
+ * Ulysses 详解", explore.n1n.ai, section "DeepSpeed-Ulysses 的核心机制：
+ * All-to-All 的艺术"):
+ *   1. seq->head exchange: P sequence shards [N/P, H, D] become one rank's
+ *      head slice [N, H/P, D]  (ul_seq_to_head);
+ *   2. causal attention over the whole sequence for that rank's heads, with
+ *      grouped-query heads and documents packed into one sequence, masked
+ *      from position ids instead of a 4-D mask (page "Ulysses verteilt
+ *      Millionen-Token-Kontexte auf mehrere GPUs", dailytechsnack.ch, section
+ *      "Integration in den Hugging-Face-Stack")  (ul_attn_fwd, ul_attn_bwd);
+ *   3. head->seq exchange, the inverse of step 1  (ul_head_to_seq).
+ * On one GPU the exchange is the local permutation that pack -> all-to-all
+ * -> unpack delivers to one rank; no collective is issued.
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major memory,
+ *    16-byte aligned (position_ids: 4-byte aligned).  The caller owns every
+ *    buffer, including the workspace; the library never allocates, frees or
+ *    keeps memory between calls.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work and return; results are ready when the stream is synchronised.
+ *  - All argument checks run before anything is enqueued.  A failed check
+ *    returns UL_ERR_ARG or UL_ERR_UNSUPPORTED, enqueues nothing and leaves
+ *    every output untouched; ul_last_error() then describes it.  A failed
+ *    kernel launch returns UL_ERR_HIP.  Device faults surface at the caller's
+ *    next synchronisation, as for any HIP work.
+ *  - Outputs never alias inputs.
+ *  - Element types: UL_BF16 (bfloat16) or UL_F32 (float).
+ */
+#ifndef UL_H
+#define UL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  UL_OK = 0,
+  UL_ERR_ARG = 1,         /* invalid shape, pointer, alignment, rank or workspace size */
+  UL_ERR_UNSUPPORTED = 2, /* valid but not implemented (head dim, dtype, group size) */
+  UL_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+} ul_status;
+
+typedef enum { UL_F32 = 0, UL_BF16 = 1 } ul_dtype;
+
+/*
+ * Step 1, seq->head exchange of rank `rank` (pages: nmedialink.com
+ * "Ulysses的工作原理" steps 1 and 3; explore.n1n.ai "核心机制" steps 1 and 3).
+ *   x_seq  [N][H][D]   the P sequence shards stacked in shard order; shard i
+ *                      holds tokens [i*N/P, (i+1)*N/P).  Read only.
+ *   x_head [N][H/P][D] written: x_head[s][k][:] = x_seq[s][rank*H/P + k][:].
+ * A bit-exact copy for any element bits.  Errors (UL_ERR_ARG): N < 1,
+ * H < 1, D < 1, P < 1, N % P != 0 (sequence length must divide by the rank
+ * count: dailytechsnack.ch "Integration in den Hugging-Face-Stack"),
+ * H % P != 0 (the degree must divide the head count: explore.n1n.ai
+ * "实践指南"), rank outside [0, P), null or misaligned pointer, overlapping
+ * buffers.
+ */
+ul_status ul_seq_to_head(const void *x_seq, void *x_head, int64_t N, int32_t H, int32_t D,
+                         int32_t P, int32_t rank, ul_dtype dt, void *stream);
+
+/*
+ * Step 3, head->seq exchange of rank `rank`, the inverse of step 1 (pages:
+ * nmedialink.com "Ulysses的工作原理" step 5; explore.n1n.ai "核心机制" step 5).
+ *   x_head [N][H/P][D] read only.
+ *   x_seq  [N][H][D]   only the head columns [rank*H/P, (rank+1)*H/P) are
+ *                      written; every other byte is left untouched, so the
+ *                      P ranks' calls together fill the tensor.
+ * Same errors as ul_seq_to_head.  The backward pass uses the same two calls:
+ * dO goes seq->head, dQ/dK/dV go head->seq (the adjoint of an all-to-all is
+ * the inverse all-to-all).
+ */
+ul_status ul_head_to_seq(const void *x_head, void *x_seq, int64_t N, int32_t H, int32_t D,
+                         int32_t P, int32_t rank, ul_dtype dt, void *stream);
+
+/*
+ * Document bounds of a packed sequence (page dailytechsnack.ch "Integration
+ * in den Hugging-Face-Stack": position ids replace the 4-D mask).  A token
+ * whose position id is 0 starts a document; token 0 always starts one; no
+ * other value starts one.
+ *   position_ids [N] int32, or NULL for one document 0..N-1.
+ *   doc_start [N], doc_end [N] int32, written: first and last token of the
+ *   token's document (inclusive).
+ *   ws / ws_bytes: device scratch of at least ul_doc_bounds_workspace_bytes(N)
+ *   bytes (8 bytes per 1024 tokens).
+ * Errors (UL_ERR_ARG): N < 1 or N >= 2^31, null or misaligned output or
+ * workspace, workspace too small, overlapping buffers.
+ */
+size_t ul_doc_bounds_workspace_bytes(int64_t N);
+ul_status ul_doc_bounds(const int32_t *position_ids, int32_t *doc_start, int32_t *doc_end,
+                        int64_t N, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Workspace bytes ul_attn_fwd (for_bwd = 0) or ul_attn_bwd (for_bwd = 1)
+ * needs for these shapes.  Linear in N (never N^2).  Returns 0 for shapes
+ * the calls would reject.
+ */
+size_t ul_attn_workspace_bytes(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, ul_dtype dt,
+                               int32_t for_bwd);
+
+/*
+ * Step 2, forward: rank-local causal attention over the whole sequence for
+ * Hq query heads and Hkv KV heads (pages: nmedialink.com "Ulysses的工作原理"
+ * step 4; explore.n1n.ai "核心机制" step 4).  Query head h reads KV head
+ * h / (Hq/Hkv).  Key j is visible to query i iff j <= i and both lie in the
+ * same document of `position_ids` (dailytechsnack.ch "Integration in den
+ * Hugging-Face-Stack").
+ *   q [N][Hq][D], k/v [N][Hkv][D] of type dt, read only.
+ *   position_ids [N] int32 or NULL (one document).
+ *   o   [N][Hq][D] of type dt, written: softmax(scale q k^T + mask) v.
+ *   lse [Hq][N] float, written: natural log of sum_j exp(scale q_i.k_j) over
+ *       the visible keys (kept for the backward pass).
+ *   scale: logit scale (pass 1/sqrt(D) for the usual attention).
+ *   ws / ws_bytes: caller-owned device workspace of at least
+ *       ul_attn_workspace_bytes(N, Hq, Hkv, D, dt, 0) bytes.
+ * bf16 inputs are multiplied on MFMA with fp32 accumulation and fp32 softmax;
+ * the probabilities are rounded to bf16 before the P.V product.
+ * Errors: UL_ERR_ARG for N < 1, Hq < 1, Hkv < 1, Hq % Hkv != 0, null or
+ * misaligned pointer, workspace too small, non-finite or non-positive scale;
+ * UL_ERR_UNSUPPORTED for D not in {64, 128}, dtype not in {UL_F32, UL_BF16},
+ * or (bf16) a group size Hq/Hkv that is not a power of two up to 16.
+ */
+ul_status ul_attn_fwd(const void *q, const void *k, const void *v, const int32_t *position_ids,
+                      void *o, float *lse, int64_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                      float scale, ul_dtype dt, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Step 2, backward of L = sum(dO * O) for the forward above.  The pages do
+ * not describe the backward; it is the chain rule with P recomputed from the
+ * saved lse:  dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
+ * dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO, with dK and dV summed over
+ * the query heads of a group.
+ *   q, k, v, position_ids, scale: as given to ul_attn_fwd.
+ *   o [N][Hq][D] and lse [Hq][N]: the forward's outputs.
+ *   dout [N][Hq][D] of type dt: gradient of L with respect to o.
+ *   dq [N][Hq][D], dk/dv [N][Hkv][D]: float, fully overwritten.
+ *   ws / ws_bytes: at least ul_attn_workspace_bytes(N, Hq, Hkv, D, dt, 1).
+ * Deterministic: the same inputs give bit-identical outputs.
+ * Errors: as ul_attn_fwd.
+ */
+ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, const int32_t *position_ids, float *dq,
+                      float *dk, float *dv, int64_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                      float scale, ul_dtype dt, void *ws, size_t ws_bytes, void *stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char *ul_last_error(void);
+
+/* Library version string. */
+const char *ul_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UL_H */

@@ -1,0 +1,125 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before enqueueing anything (the
+pointers below are never dereferenced because every call fails a check first).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import ulysses_sequence_parallelism_ul_amd as ul
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ul.h")
+
+# fake, 256-byte aligned, never dereferenced
+A, B, C, D_, E, F, G_, H_, I_, J = (0x10000000 * (i + 1) for i in range(10))
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ul_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ul.load()
+    syms = declared_symbols()
+    assert len(syms) >= 9
+    for s in syms:
+        assert hasattr(lib, s), s
+        assert s in ul.SIGNATURES, s
+    assert set(ul.SIGNATURES) == set(syms)
+
+
+def test_version_and_clean_error():
+    assert "gfx950" in ul.version()
+
+
+def _err():
+    return ul.load().ul_last_error().decode()
+
+
+def test_relayout_rejections():
+    lib = ul.load()
+    P = ctypes.c_void_p
+    # N % P
+    assert lib.ul_seq_to_head(A, B, 10, 8, 64, 4, 0, ul.UL_BF16, None) == ul.UL_ERR_ARG
+    assert "divisible" in _err()
+    # H % P
+    assert lib.ul_seq_to_head(A, B, 16, 6, 64, 4, 0, ul.UL_BF16, None) == ul.UL_ERR_ARG
+    # rank out of range
+    assert lib.ul_head_to_seq(A, B, 16, 8, 64, 4, 4, ul.UL_BF16, None) == ul.UL_ERR_ARG
+    assert lib.ul_head_to_seq(A, B, 16, 8, 64, 4, -1, ul.UL_BF16, None) == ul.UL_ERR_ARG
+    # null and misaligned pointers
+    assert lib.ul_seq_to_head(None, B, 16, 8, 64, 4, 0, ul.UL_BF16, None) == ul.UL_ERR_ARG
+    assert lib.ul_seq_to_head(A + 2, B, 16, 8, 64, 4, 0, ul.UL_BF16, None) == ul.UL_ERR_ARG
+    # overlapping buffers
+    assert lib.ul_seq_to_head(A, A + 256, 16, 8, 64, 4, 0, ul.UL_BF16, None) == ul.UL_ERR_ARG
+    assert "overlap" in _err()
+    # N < 1, P < 1, bad dtype
+    assert lib.ul_seq_to_head(A, B, 0, 8, 64, 4, 0, ul.UL_BF16, None) == ul.UL_ERR_ARG
+    assert lib.ul_seq_to_head(A, B, 16, 8, 64, 0, 0, ul.UL_BF16, None) == ul.UL_ERR_ARG
+    assert lib.ul_seq_to_head(A, B, 16, 8, 64, 4, 0, 7, None) == ul.UL_ERR_UNSUPPORTED
+
+
+def test_doc_bounds_rejections():
+    lib = ul.load()
+    assert lib.ul_doc_bounds_workspace_bytes(1) == 8
+    assert lib.ul_doc_bounds_workspace_bytes(1025) == 16
+    assert lib.ul_doc_bounds(A, B, C, 0, D_, 8, None) == ul.UL_ERR_ARG
+    assert lib.ul_doc_bounds(A, None, C, 16, D_, 8, None) == ul.UL_ERR_ARG
+    assert lib.ul_doc_bounds(A, B, C, 16, D_, 4, None) == ul.UL_ERR_ARG  # workspace too small
+    assert lib.ul_doc_bounds(A + 2, B, C, 16, D_, 8, None) == ul.UL_ERR_ARG  # misaligned ids
+    assert lib.ul_doc_bounds(A, A, C, 16, D_, 8, None) == ul.UL_ERR_ARG  # ids overlap output
+
+
+def test_workspace_is_linear_in_n():
+    lib = ul.load()
+    for dt in (ul.UL_BF16, ul.UL_F32):
+        for bwd in (0, 1):
+            w1 = lib.ul_attn_workspace_bytes(1 << 16, 4, 1, 128, dt, bwd)
+            w2 = lib.ul_attn_workspace_bytes(1 << 17, 4, 1, 128, dt, bwd)
+            assert w1 > 0 and abs(w2 - 2 * w1) <= 4096
+    # rejected shapes report 0
+    assert lib.ul_attn_workspace_bytes(1024, 6, 4, 128, ul.UL_BF16, 0) == 0
+    assert lib.ul_attn_workspace_bytes(1024, 4, 1, 96, ul.UL_BF16, 0) == 0
+    assert lib.ul_attn_workspace_bytes(0, 4, 1, 128, ul.UL_BF16, 0) == 0
+
+
+def _fwd(lib, N=64, Hq=4, Hkv=1, D=128, scale=0.1, dt=ul.UL_BF16, ws=F, wsb=1 << 30, q=A, o=D_, pos=None):
+    return lib.ul_attn_fwd(q, B, C, pos, o, E, N, Hq, Hkv, D, scale, dt, ws, wsb, None)
+
+
+def test_attn_fwd_rejections():
+    lib = ul.load()
+    assert _fwd(lib, Hq=6, Hkv=4) == ul.UL_ERR_ARG
+    assert "multiple" in _err()
+    assert _fwd(lib, D=96) == ul.UL_ERR_UNSUPPORTED
+    assert _fwd(lib, Hq=12, Hkv=4) == ul.UL_ERR_UNSUPPORTED  # bf16 group of 3
+    assert _fwd(lib, Hq=64, Hkv=2) == ul.UL_ERR_UNSUPPORTED  # bf16 group of 32
+    assert _fwd(lib, N=0) == ul.UL_ERR_ARG
+    assert _fwd(lib, scale=0.0) == ul.UL_ERR_ARG
+    assert _fwd(lib, scale=float("nan")) == ul.UL_ERR_ARG
+    assert _fwd(lib, wsb=100) == ul.UL_ERR_ARG
+    assert "workspace" in _err()
+    assert _fwd(lib, q=None) == ul.UL_ERR_ARG
+    assert _fwd(lib, q=A + 8) == ul.UL_ERR_ARG
+    assert _fwd(lib, o=A) == ul.UL_ERR_ARG  # output aliases q
+    assert _fwd(lib, pos=G_ + 2) == ul.UL_ERR_ARG
+    assert _fwd(lib, dt=5) == ul.UL_ERR_UNSUPPORTED
+
+
+def test_attn_bwd_rejections():
+    lib = ul.load()
+
+    def bwd(N=64, Hq=4, Hkv=1, D=128, wsb=1 << 30, dq=G_, dk=H_):
+        return lib.ul_attn_bwd(A, B, C, D_, E, F, None, dq, dk, I_, N, Hq, Hkv, D, 0.1, ul.UL_BF16, J, wsb, None)
+
+    assert bwd(Hq=5, Hkv=2) == ul.UL_ERR_ARG
+    assert bwd(D=32) == ul.UL_ERR_UNSUPPORTED
+    assert bwd(wsb=16) == ul.UL_ERR_ARG
+    assert bwd(dq=None) == ul.UL_ERR_ARG
+    assert bwd(dk=G_) == ul.UL_ERR_ARG  # dk overlaps dq

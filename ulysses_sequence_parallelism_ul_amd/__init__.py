@@ -1,0 +1,222 @@
+"""Python binding of libul, the MI355X (gfx950) per-rank hot path of Ulysses
+sequence parallelism: the seq->head exchange, causal packed-document
+grouped-query attention forward and backward, and the head->seq exchange.
+
+This module only marshals arguments: it checks torch tensors, allocates
+outputs and workspaces with torch on the tensors' device, and calls the C ABI
+(include/ul.h) on torch's current HIP stream.  Every step of the path runs in
+the library's HIP kernels; there is no CPU or PyTorch fallback, and a missing
+library raises.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "UlError",
+    "load",
+    "library_path",
+    "version",
+    "seq_to_head",
+    "head_to_seq",
+    "doc_bounds",
+    "attn_workspace_bytes",
+    "attn_fwd",
+    "attn_bwd",
+    "UL_OK",
+    "UL_ERR_ARG",
+    "UL_ERR_UNSUPPORTED",
+    "UL_ERR_HIP",
+    "UL_F32",
+    "UL_BF16",
+]
+
+UL_OK, UL_ERR_ARG, UL_ERR_UNSUPPORTED, UL_ERR_HIP = 0, 1, 2, 3
+UL_F32, UL_BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libul.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/ul.h
+SIGNATURES = {
+    "ul_seq_to_head": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P]),
+    "ul_head_to_seq": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P]),
+    "ul_doc_bounds_workspace_bytes": (_SZ, [_I64]),
+    "ul_doc_bounds": (_I32, [_P, _P, _P, _I64, _P, _SZ, _P]),
+    "ul_attn_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32]),
+    "ul_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
+    "ul_attn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
+    "ul_last_error": (ctypes.c_char_p, []),
+    "ul_version": (ctypes.c_char_p, []),
+}
+
+
+class UlError(RuntimeError):
+    """A non-OK status from libul; ``status`` holds the ul_status code."""
+
+    def __init__(self, status, message):
+        super().__init__(f"libul status {status}: {message}")
+        self.status = status
+
+
+def load():
+    """Load libul.so (built in-tree by ``build.build()``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is not built; run `python -m ulysses_sequence_parallelism_ul_amd.build` "
+                "(there is no fallback path)")
+        lib = ctypes.CDLL(library_path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def version():
+    return load().ul_version().decode()
+
+
+def _check(status):
+    if status != UL_OK:
+        raise UlError(status, load().ul_last_error().decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return UL_BF16
+    if t.dtype == torch.float32:
+        return UL_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def seq_to_head(x_seq, P, rank, out=None):
+    """[N, H, D] stacked sequence shards -> rank's head slice [N, H/P, D] (bit-exact)."""
+    lib = load()
+    N, H, D = x_seq.shape
+    if out is None:
+        if H % P:
+            raise ValueError(f"H={H} is not divisible by P={P}")
+        out = torch.empty((N, H // P, D), dtype=x_seq.dtype, device=x_seq.device)
+    if out.dtype != x_seq.dtype:
+        raise TypeError("out dtype differs from x_seq")
+    _check(lib.ul_seq_to_head(_dev(x_seq, "x_seq"), _dev(out, "out"), N, H, D, P, rank, _dtype_code(x_seq),
+                              _stream(x_seq.device)))
+    return out
+
+
+def head_to_seq(x_head, x_seq, P, rank):
+    """Write rank's head slice [N, H/P, D] into columns of x_seq [N, H, D] in place; returns x_seq."""
+    lib = load()
+    N, H, D = x_seq.shape
+    if x_head.dtype != x_seq.dtype:
+        raise TypeError("x_head dtype differs from x_seq")
+    if H % P or tuple(x_head.shape) != (N, H // P, D):
+        raise ValueError(f"x_head shape {tuple(x_head.shape)} does not match [N, H/P, D] for x_seq {tuple(x_seq.shape)}")
+    _check(lib.ul_head_to_seq(_dev(x_head, "x_head"), _dev(x_seq, "x_seq"), N, H, D, P, rank, _dtype_code(x_seq),
+                              _stream(x_seq.device)))
+    return x_seq
+
+
+def doc_bounds(position_ids, N=None, device=None):
+    """(doc_start, doc_end) int32 [N] from int32 position ids (None: one document of length N)."""
+    lib = load()
+    if position_ids is not None:
+        if position_ids.dtype != torch.int32:
+            raise TypeError("position_ids must be int32")
+        N = position_ids.numel()
+        device = position_ids.device
+        pptr = _dev(position_ids, "position_ids")
+    else:
+        pptr = None
+    ds = torch.empty(N, dtype=torch.int32, device=device)
+    de = torch.empty(N, dtype=torch.int32, device=device)
+    wsb = lib.ul_doc_bounds_workspace_bytes(N)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device)
+    _check(lib.ul_doc_bounds(pptr, ds.data_ptr(), de.data_ptr(), N, ws.data_ptr(), wsb, _stream(device)))
+    return ds, de
+
+
+def attn_workspace_bytes(N, Hq, Hkv, D, dtype, for_bwd):
+    code = UL_BF16 if dtype == torch.bfloat16 else UL_F32 if dtype == torch.float32 else -1
+    return load().ul_attn_workspace_bytes(N, Hq, Hkv, D, code, 1 if for_bwd else 0)
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace holds fewer than {nbytes} bytes")
+    return workspace
+
+
+def _pos_ptr(position_ids, N):
+    if position_ids is None:
+        return None
+    if position_ids.dtype != torch.int32 or position_ids.numel() != N:
+        raise ValueError("position_ids must be int32 with N elements")
+    return _dev(position_ids, "position_ids")
+
+
+def attn_fwd(q, k, v, position_ids=None, scale=None, out=None, lse=None, workspace=None):
+    """Causal packed-document GQA attention forward. Returns (o [N,Hq,D], lse [Hq,N] fp32)."""
+    lib = load()
+    N, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != N or k.shape[2] != D or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes or dtypes disagree")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    wsb = lib.ul_attn_workspace_bytes(N, Hq, Hkv, D, _dtype_code(q), 0)
+    ws = _workspace(wsb, q.device, workspace)
+    _check(lib.ul_attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _pos_ptr(position_ids, N), _dev(out, "out"),
+                           _dev(lse, "lse"), N, Hq, Hkv, D, scale, _dtype_code(q), ws.data_ptr(), wsb,
+                           _stream(q.device)))
+    return out, lse
+
+
+def attn_bwd(q, k, v, o, dout, lse, position_ids=None, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward of attn_fwd. Returns fp32 (dq [N,Hq,D], dk [N,Hkv,D], dv [N,Hkv,D])."""
+    lib = load()
+    N, Hq, D = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((N, Hq, D), **f32) if dq is None else dq
+    dk = torch.empty((N, Hkv, D), **f32) if dk is None else dk
+    dv = torch.empty((N, Hkv, D), **f32) if dv is None else dv
+    wsb = lib.ul_attn_workspace_bytes(N, Hq, Hkv, D, _dtype_code(q), 1)
+    ws = _workspace(wsb, q.device, workspace)
+    _check(lib.ul_attn_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(dout, "dout"),
+                           _dev(lse, "lse"), _pos_ptr(position_ids, N), _dev(dq, "dq"), _dev(dk, "dk"),
+                           _dev(dv, "dv"), N, Hq, Hkv, D, scale, _dtype_code(q), ws.data_ptr(), wsb,
+                           _stream(q.device)))
+    return dq, dk, dv

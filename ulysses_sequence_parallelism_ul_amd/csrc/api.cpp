@@ -1,0 +1,261 @@
+// C ABI of libul: argument validation, workspace layout and dispatch.
+// Every check runs before anything is enqueued; on failure nothing is
+// enqueued and ul_last_error() holds the reason.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ul_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ul_status fail(ul_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ul_status ok() {
+  g_err.clear();
+  return UL_OK;
+}
+
+ul_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(UL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(ul_dtype dt) { return dt == UL_BF16 ? 2 : dt == UL_F32 ? 4 : 0; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+struct Buf {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+
+// Check non-null, alignment and pairwise non-overlap of device buffers.
+ul_status check_bufs(const Buf* b, int count, uintptr_t align) {
+  for (int i = 0; i < count; ++i) {
+    if (b[i].p == nullptr) return fail(UL_ERR_ARG, "%s is NULL", b[i].name);
+    if (!aligned(b[i].p, align)) return fail(UL_ERR_ARG, "%s is not %d-byte aligned", b[i].name, (int)align);
+  }
+  for (int i = 0; i < count; ++i)
+    for (int j = i + 1; j < count; ++j)
+      if (overlap(b[i].p, b[i].n, b[j].p, b[j].n))
+        return fail(UL_ERR_ARG, "%s and %s overlap", b[i].name, b[j].name);
+  return UL_OK;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+ul_status check_relayout(const void* src, void* dst, bool seq_to_head, int64_t N, int32_t H, int32_t D, int32_t P,
+                         int32_t rank, ul_dtype dt) {
+  if (dt != UL_BF16 && dt != UL_F32) return fail(UL_ERR_UNSUPPORTED, "dtype %d is not UL_F32 or UL_BF16", (int)dt);
+  if (N < 1) return fail(UL_ERR_ARG, "N=%lld must be >= 1", (long long)N);
+  if (H < 1 || D < 1) return fail(UL_ERR_ARG, "H=%d and D=%d must be >= 1", H, D);
+  if (P < 1) return fail(UL_ERR_ARG, "P=%d must be >= 1", P);
+  if (N % P != 0) return fail(UL_ERR_ARG, "sequence length N=%lld is not divisible by P=%d", (long long)N, P);
+  if (H % P != 0) return fail(UL_ERR_ARG, "head count H=%d is not divisible by P=%d", H, P);
+  if (rank < 0 || rank >= P) return fail(UL_ERR_ARG, "rank %d outside [0, %d)", rank, P);
+  const size_t e = (size_t)elem_bytes(dt);
+  const size_t full = (size_t)N * H * D * e, part = (size_t)N * (H / P) * D * e;
+  Buf bufs[2] = {{src, seq_to_head ? full : part, seq_to_head ? "x_seq" : "x_head"},
+                 {dst, seq_to_head ? part : full, seq_to_head ? "x_head" : "x_seq"}};
+  return check_bufs(bufs, 2, 16);
+}
+
+ul_status check_attn_shapes(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, float scale, ul_dtype dt) {
+  if (dt != UL_BF16 && dt != UL_F32) return fail(UL_ERR_UNSUPPORTED, "dtype %d is not UL_F32 or UL_BF16", (int)dt);
+  if (N < 1 || N > 0x7fffffffLL) return fail(UL_ERR_ARG, "N=%lld must be in [1, 2^31)", (long long)N);
+  if (Hq < 1 || Hkv < 1) return fail(UL_ERR_ARG, "Hq=%d and Hkv=%d must be >= 1", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(UL_ERR_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (D != 64 && D != 128) return fail(UL_ERR_UNSUPPORTED, "head dim D=%d is not 64 or 128", D);
+  if (dt == UL_BF16 && !(is_pow2(Hq / Hkv) && Hq / Hkv <= 16))
+    return fail(UL_ERR_UNSUPPORTED, "bf16 attention needs a power-of-two group size <= 16, got %d", Hq / Hkv);
+  if ((int64_t)N * (Hq / Hkv) > 0x7fffffffLL) return fail(UL_ERR_ARG, "N * Hq / Hkv must be < 2^31");
+  if (!(scale > 0.0f) || !isfinite(scale)) return fail(UL_ERR_ARG, "scale must be finite and > 0");
+  return UL_OK;
+}
+
+}  // namespace
+
+namespace ul {
+
+WsLayout ws_layout(int64_t N, int Hq, int Hkv, int D, ul_dtype dt, bool for_bwd) {
+  WsLayout L;
+  const size_t A = 256;
+  const int64_t G = Hq / Hkv;
+  const int64_t nblk = (N + kScanBlock - 1) / kScanBlock;
+  const int64_t NB = (N + kTB - 1) / kTB;
+  const int64_t CB = (N * G + kTB - 1) / kTB;
+  size_t off = 0;
+  L.doc_start = off; off = align_up(off + (size_t)N * 4, A);
+  L.doc_end = off;   off = align_up(off + (size_t)N * 4, A);
+  L.scan = off;      off = align_up(off + (size_t)nblk * 8, A);
+  if (dt == UL_BF16 && !for_bwd) {
+    L.vt = off; off = align_up(off + (size_t)Hkv * NB * D * kTB * 2, A);
+  }
+  if (for_bwd) {
+    L.delta = off; off = align_up(off + (size_t)Hq * N * 4, A);
+    if (dt == UL_BF16) {
+      L.qt = off;  off = align_up(off + (size_t)Hkv * CB * D * kTB * 2, A);
+      L.dot = off; off = align_up(off + (size_t)Hkv * CB * D * kTB * 2, A);
+      L.kt = off;  off = align_up(off + (size_t)Hkv * NB * D * kTB * 2, A);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace ul
+
+extern "C" {
+
+const char* ul_last_error(void) { return g_err.c_str(); }
+
+const char* ul_version(void) { return "ulysses-mi355x 0.1 (gfx950)"; }
+
+ul_status ul_seq_to_head(const void* x_seq, void* x_head, int64_t N, int32_t H, int32_t D, int32_t P, int32_t rank,
+                         ul_dtype dt, void* stream) {
+  ul_status st = check_relayout(x_seq, x_head, true, N, H, D, P, rank, dt);
+  if (st != UL_OK) return st;
+  return hip_status(ul::launch_relayout(x_seq, x_head, N, H, D, P, rank, elem_bytes(dt), true, (hipStream_t)stream),
+                    "seq_to_head launch");
+}
+
+ul_status ul_head_to_seq(const void* x_head, void* x_seq, int64_t N, int32_t H, int32_t D, int32_t P, int32_t rank,
+                         ul_dtype dt, void* stream) {
+  ul_status st = check_relayout(x_head, x_seq, false, N, H, D, P, rank, dt);
+  if (st != UL_OK) return st;
+  return hip_status(ul::launch_relayout(x_head, x_seq, N, H, D, P, rank, elem_bytes(dt), false, (hipStream_t)stream),
+                    "head_to_seq launch");
+}
+
+size_t ul_doc_bounds_workspace_bytes(int64_t N) {
+  if (N < 1 || N > 0x7fffffffLL) return 0;
+  return (size_t)((N + ul::kScanBlock - 1) / ul::kScanBlock) * 8;
+}
+
+ul_status ul_doc_bounds(const int32_t* position_ids, int32_t* doc_start, int32_t* doc_end, int64_t N, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (N < 1 || N > 0x7fffffffLL) return fail(UL_ERR_ARG, "N=%lld must be in [1, 2^31)", (long long)N);
+  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  const size_t need = ul_doc_bounds_workspace_bytes(N);
+  Buf bufs[3] = {{doc_start, (size_t)N * 4, "doc_start"}, {doc_end, (size_t)N * 4, "doc_end"}, {ws, need, "ws"}};
+  ul_status st = check_bufs(bufs, 3, 4);
+  if (st != UL_OK) return st;
+  if (ws_bytes < need) return fail(UL_ERR_ARG, "workspace of %zu bytes is smaller than %zu", ws_bytes, need);
+  if (position_ids && (overlap(position_ids, (size_t)N * 4, doc_start, (size_t)N * 4) ||
+                       overlap(position_ids, (size_t)N * 4, doc_end, (size_t)N * 4)))
+    return fail(UL_ERR_ARG, "position_ids overlaps an output");
+  return hip_status(ul::launch_doc_bounds(position_ids, doc_start, doc_end, static_cast<int32_t*>(ws), (int)N,
+                                          (hipStream_t)stream),
+                    "doc_bounds launch");
+}
+
+size_t ul_attn_workspace_bytes(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, ul_dtype dt, int32_t for_bwd) {
+  std::string saved = g_err;
+  ul_status st = check_attn_shapes(N, Hq, Hkv, D, 1.0f, dt);
+  g_err = saved;
+  if (st != UL_OK) return 0;
+  return ul::ws_layout(N, Hq, Hkv, D, dt, for_bwd != 0).total;
+}
+
+ul_status ul_attn_fwd(const void* q, const void* k, const void* v, const int32_t* position_ids, void* o, float* lse,
+                      int64_t N, int32_t Hq, int32_t Hkv, int32_t D, float scale, ul_dtype dt, void* ws,
+                      size_t ws_bytes, void* stream) {
+  ul_status st = check_attn_shapes(N, Hq, Hkv, D, scale, dt);
+  if (st != UL_OK) return st;
+  const size_t e = (size_t)elem_bytes(dt);
+  const ul::WsLayout L = ul::ws_layout(N, Hq, Hkv, D, dt, false);
+  const size_t nq = (size_t)N * Hq * D * e, nkv = (size_t)N * Hkv * D * e;
+  Buf bufs[6] = {{q, nq, "q"}, {k, nkv, "k"}, {v, nkv, "v"}, {o, nq, "o"}, {lse, (size_t)Hq * N * 4, "lse"},
+                 {ws, L.total, "ws"}};
+  // q, k, v may alias each other (read only); outputs and workspace may not alias anything
+  for (int i = 0; i < 6; ++i) {
+    if (bufs[i].p == nullptr) return fail(UL_ERR_ARG, "%s is NULL", bufs[i].name);
+    if (!aligned(bufs[i].p, 16)) return fail(UL_ERR_ARG, "%s is not 16-byte aligned", bufs[i].name);
+  }
+  for (int i = 3; i < 6; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (i != j && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
+        return fail(UL_ERR_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
+  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  if (ws_bytes < L.total) return fail(UL_ERR_ARG, "workspace of %zu bytes is smaller than %zu", ws_bytes, L.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  int32_t* ds = reinterpret_cast<int32_t*>(w + L.doc_start);
+  int32_t* de = reinterpret_cast<int32_t*>(w + L.doc_end);
+  hipError_t err = ul::launch_doc_bounds(position_ids, ds, de, reinterpret_cast<int32_t*>(w + L.scan), (int)N, s);
+  if (err != hipSuccess) return hip_status(err, "doc_bounds launch");
+  if (dt == UL_BF16)
+    err = ul::launch_attn_fwd_bf16(static_cast<const ul::bf16*>(q), static_cast<const ul::bf16*>(k),
+                                   static_cast<const ul::bf16*>(v), ds, static_cast<ul::bf16*>(o), lse,
+                                   reinterpret_cast<ul::bf16*>(w + L.vt), (int)N, Hq, Hkv, D, scale, s);
+  else
+    err = ul::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                  static_cast<const float*>(v), ds, static_cast<float*>(o), lse, (int)N, Hq, Hkv, D,
+                                  scale, s);
+  return hip_status(err, "attn_fwd launch");
+}
+
+ul_status ul_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      const int32_t* position_ids, float* dq, float* dk, float* dv, int64_t N, int32_t Hq,
+                      int32_t Hkv, int32_t D, float scale, ul_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  ul_status st = check_attn_shapes(N, Hq, Hkv, D, scale, dt);
+  if (st != UL_OK) return st;
+  const size_t e = (size_t)elem_bytes(dt);
+  const ul::WsLayout L = ul::ws_layout(N, Hq, Hkv, D, dt, true);
+  const size_t nq = (size_t)N * Hq * D * e, nkv = (size_t)N * Hkv * D * e;
+  const size_t fq = (size_t)N * Hq * D * 4, fkv = (size_t)N * Hkv * D * 4;
+  Buf bufs[10] = {{q, nq, "q"},   {k, nkv, "k"},   {v, nkv, "v"},   {o, nq, "o"},   {dout, nq, "dout"},
+                  {lse, (size_t)Hq * N * 4, "lse"}, {dq, fq, "dq"}, {dk, fkv, "dk"}, {dv, fkv, "dv"},
+                  {ws, L.total, "ws"}};
+  for (int i = 0; i < 10; ++i) {
+    if (bufs[i].p == nullptr) return fail(UL_ERR_ARG, "%s is NULL", bufs[i].name);
+    if (!aligned(bufs[i].p, 16)) return fail(UL_ERR_ARG, "%s is not 16-byte aligned", bufs[i].name);
+  }
+  for (int i = 6; i < 10; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (i != j && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
+        return fail(UL_ERR_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
+  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  if (ws_bytes < L.total) return fail(UL_ERR_ARG, "workspace of %zu bytes is smaller than %zu", ws_bytes, L.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  int32_t* ds = reinterpret_cast<int32_t*>(w + L.doc_start);
+  int32_t* de = reinterpret_cast<int32_t*>(w + L.doc_end);
+  hipError_t err = ul::launch_doc_bounds(position_ids, ds, de, reinterpret_cast<int32_t*>(w + L.scan), (int)N, s);
+  if (err != hipSuccess) return hip_status(err, "doc_bounds launch");
+  float* delta = reinterpret_cast<float*>(w + L.delta);
+  if (dt == UL_BF16)
+    err = ul::launch_attn_bwd_bf16(
+        static_cast<const ul::bf16*>(q), static_cast<const ul::bf16*>(k), static_cast<const ul::bf16*>(v),
+        static_cast<const ul::bf16*>(o), static_cast<const ul::bf16*>(dout), lse, ds, de, dq, dk, dv, delta,
+        reinterpret_cast<ul::bf16*>(w + L.qt), reinterpret_cast<ul::bf16*>(w + L.dot),
+        reinterpret_cast<ul::bf16*>(w + L.kt), (int)N, Hq, Hkv, D, scale, s);
+  else
+    err = ul::launch_attn_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                  static_cast<const float*>(v), static_cast<const float*>(o),
+                                  static_cast<const float*>(dout), lse, ds, de, dq, dk, dv, delta, (int)N, Hq, Hkv,
+                                  D, scale, s);
+  if (err == hipErrorNotSupported) return fail(UL_ERR_UNSUPPORTED, "attn_bwd: this configuration is not built");
+  return hip_status(err, "attn_bwd launch");
+}
+
+}  // extern "C"

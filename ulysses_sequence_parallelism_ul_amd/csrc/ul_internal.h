@@ -1,0 +1,68 @@
+// Internal declarations shared by the HIP translation units of libul.
+// Nothing here is part of the C ABI (include/ul.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ul.h"
+
+namespace ul {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Tokens per tile of the transposed (blocked) operand copies kept in the
+// workspace: element (col, d) of a [cols][D] matrix lives at
+// [col / kTB][d][col % kTB].
+constexpr int kTB = 64;
+// Tokens per block of the document-bounds scan.
+constexpr int kScanBlock = 1024;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Byte offsets of the workspace regions of ul_attn_fwd / ul_attn_bwd.
+struct WsLayout {
+  size_t doc_start = 0, doc_end = 0, scan = 0;  // int32 [N], int32 [N], int32 [2 * nblk]
+  size_t vt = 0;     // bf16 fwd: V^T blocked [Hkv][NB][D][kTB]
+  size_t delta = 0;  // bwd: float [Hkv][N*G] (query-column order)
+  size_t qt = 0;     // bf16 bwd: Q^T blocked  [Hkv][CB][D][kTB]
+  size_t dot = 0;    // bf16 bwd: dO^T blocked [Hkv][CB][D][kTB]
+  size_t kt = 0;     // bf16 bwd: K^T blocked  [Hkv][NB][D][kTB]
+  size_t total = 0;
+};
+
+WsLayout ws_layout(int64_t N, int Hq, int Hkv, int D, ul_dtype dt, bool for_bwd);
+
+// ---- launchers (enqueue only; arguments already validated) ----
+hipError_t launch_relayout(const void* src, void* dst, int64_t N, int H, int D, int P, int rank,
+                           int elem_bytes, bool seq_to_head, hipStream_t s);
+hipError_t launch_doc_bounds(const int32_t* pos, int32_t* doc_start, int32_t* doc_end,
+                             int32_t* scan_scratch, int N, hipStream_t s);
+// [cols][D] bf16 view (column c -> token c >> lgG, head (hk << lgG) + (c & (G-1)) of a
+// [N][H][D] tensor) -> blocked transpose [Hkv][ceil(ncols / kTB)][D][kTB], zero-padded.
+hipError_t launch_transpose_blocked(const bf16* src, bf16* dst, int64_t ncols, int H, int Hkv, int lgG, int D,
+                                    hipStream_t s);
+hipError_t launch_attn_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* doc_start,
+                                bf16* o, float* lse, bf16* vt_ws, int N, int Hq, int Hkv, int D,
+                                float scale, hipStream_t s);
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* doc_start,
+                               float* o, float* lse, int N, int Hq, int Hkv, int D, float scale,
+                               hipStream_t s);
+hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
+                                const bf16* dout, const float* lse, const int32_t* doc_start,
+                                const int32_t* doc_end, float* dq, float* dk, float* dv, float* delta,
+                                bf16* qt, bf16* dot, bf16* kt, int N, int Hq, int Hkv, int D,
+                                float scale, hipStream_t s);
+hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                               const float* dout, const float* lse, const int32_t* doc_start,
+                               const int32_t* doc_end, float* dq, float* dk, float* dv, float* delta,
+                               int N, int Hq, int Hkv, int D, float scale, hipStream_t s);
+
+}  // namespace ul
