@@ -151,6 +151,24 @@ ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o
                       float *dk, float *dv, int64_t N, int32_t Hq, int32_t Hkv, int32_t D,
                       float scale, ul_dtype dt, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Optional per-kernel timing for benchmarks.  While enabled, every kernel the
+ * library launches is bracketed by two hipEvents recorded on the kernel's own
+ * stream; elapsed times are summed per kernel name.  Off by default.
+ *   ul_timing_enable(on): switch on (1) or off (0); returns the previous state.
+ *   ul_timing_reset(): wait for pending events and clear the totals.
+ *   ul_timing_read(index, name, name_len, total_ms, launches): waits for
+ *     pending events; for index < 0 returns the number of kernel names; for
+ *     0 <= index < count copies the index-th name (NUL-terminated, truncated
+ *     to name_len) and its summed milliseconds and launch count, and returns
+ *     the count; returns -1 for an index out of range or a HIP event error.
+ * Host memory only; no device memory is allocated (events are HIP events).
+ */
+int32_t ul_timing_enable(int32_t on);
+void ul_timing_reset(void);
+int32_t ul_timing_read(int32_t index, char *name, size_t name_len, double *total_ms,
+                       int64_t *launches);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *ul_last_error(void);
 

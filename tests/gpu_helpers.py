@@ -9,6 +9,14 @@ TOL_OUT = 2e-2
 TOL_LSE = 1e-3
 
 
+def grad_bar(ref):
+    """Gradient bar: 2e-2 absolute while |ref| <= 8 (the regime of the 4 q / 1 KV
+    workloads), then the same relative error (2e-2 / 8 = 2.5e-3, about one bf16
+    half-ulp of the probabilities) for larger gradients, which arise with larger
+    query groups summing into one KV head."""
+    return TOL_OUT * max(1.0, float(np.abs(ref).max()) / 8.0)
+
+
 def require_gpu():
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")

@@ -1,0 +1,141 @@
+"""The whole per-rank path at full size: seq->head, attention forward and
+backward, head->seq, for the packed training share (N=262144) and the
+million-token share (N=1048576), bf16, 8 emulated ranks, rank 0.
+
+Checks: exchanges bit-exact on full tensors against a torch slice (an
+independent library routine) and on sampled rows against the oracle; forward
+and dQ on sampled rows against the oracle; dK/dV on the last keys of
+documents against the oracle; per-document dK/dV sums; the Q = 0 closed forms
+at N = 1M; determinism.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ulysses_sequence_parallelism_ul_amd as ul
+from gpu_helpers import TOL_LSE, TOL_OUT, log, max_abs, np64, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+P, RANK = 8, 0
+
+
+def _run(name, zero_q=False):
+    w = synth.WORKLOADS[name]
+    N, D = w["N"], w["D"]
+    dev = torch.device("cuda:0")
+    seed = w["index"]
+    q_seq = synth.device_normal((N, w["Hq"], D), seed, 1, dev, torch.bfloat16)
+    k_seq = synth.device_normal((N, w["Hkv"], D), seed, 2, dev, torch.bfloat16)
+    v_seq = synth.device_normal((N, w["Hkv"], D), seed, 3, dev, torch.bfloat16)
+    do_seq = synth.device_normal((N, w["Hq"], D), seed, 4, dev, torch.bfloat16)
+    if zero_q:
+        q_seq.zero_()
+    pos_np = synth.workload_positions(name)
+    pos = torch.from_numpy(pos_np).to(dev)
+    q, k, v, do = (ul.seq_to_head(x, P, RANK) for x in (q_seq, k_seq, v_seq, do_seq))
+    o, lse = ul.attn_fwd(q, k, v, pos)
+    dq, dk, dv = ul.attn_bwd(q, k, v, o, do, lse, pos)
+    o_seq = torch.zeros_like(q_seq)
+    dq_seq = torch.zeros(q_seq.shape, dtype=torch.float32, device=dev)
+    dk_seq = torch.zeros(k_seq.shape, dtype=torch.float32, device=dev)
+    dv_seq = torch.zeros(k_seq.shape, dtype=torch.float32, device=dev)
+    ul.head_to_seq(o, o_seq, P, RANK)
+    ul.head_to_seq(dq, dq_seq, P, RANK)
+    ul.head_to_seq(dk, dk_seq, P, RANK)
+    ul.head_to_seq(dv, dv_seq, P, RANK)
+    torch.cuda.synchronize()
+    return dict(N=N, D=D, pos=pos_np, q_seq=q_seq, k_seq=k_seq, v_seq=v_seq, do_seq=do_seq, q=q, k=k, v=v, do=do,
+                o=o, lse=lse, dq=dq, dk=dk, dv=dv, o_seq=o_seq, dq_seq=dq_seq, dk_seq=dk_seq, dv_seq=dv_seq)
+
+
+def _check_exchanges(r):
+    hq = r["q"].shape[1]
+    hkv = r["k"].shape[1]
+    for full, part, hp in ((r["q_seq"], r["q"], hq), (r["k_seq"], r["k"], hkv), (r["v_seq"], r["v"], hkv),
+                           (r["do_seq"], r["do"], hq)):
+        assert torch.equal(part.view(torch.int16), full[:, RANK * hp:(RANK + 1) * hp].contiguous().view(torch.int16))
+    for full, part, hp in ((r["o_seq"], r["o"], hq), (r["dq_seq"], r["dq"], hq), (r["dk_seq"], r["dk"], hkv),
+                           (r["dv_seq"], r["dv"], hkv)):
+        assert torch.equal(full[:, RANK * hp:(RANK + 1) * hp], part)
+        assert torch.count_nonzero(full[:, (RANK + 1) * hp:]) == 0
+    # oracle on a row sample of the raw bits
+    rows = torch.arange(0, 64, device="cuda:0")
+    bits = r["q_seq"][rows].view(torch.int16).cpu().numpy()
+    np.testing.assert_array_equal(r["q"][rows].view(torch.int16).cpu().numpy(), oracle.seq_to_head(bits, P, RANK))
+
+
+def _host(r):
+    return (r["q"].float().cpu().numpy(), r["k"].double().cpu().numpy(), r["v"].double().cpu().numpy(),
+            r["do"].float().cpu().numpy())
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", ["train_packed", "million"])
+def test_full_path(name):
+    require_gpu()
+    log(f"path {name}")
+    r = _run(name)
+    _check_exchanges(r)
+    N, pos = r["N"], r["pos"]
+    pos_o = None if name == "million" else pos  # million: one document (ids 0..N-1)
+    qf, k64, v64, dof = _host(r)
+    rng = np.random.Generator(np.random.PCG64(11))
+    rows = np.unique(np.r_[0:16, N - 16:N, rng.integers(0, N, 16), 63, 64, 65, 4095, 4096])
+    log(f"path {name}: oracle forward rows")
+    rr, eo, el = oracle.attn_fwd_rows(qf, k64, v64, pos_o, rows)
+    ri = torch.from_numpy(rr).to("cuda:0")
+    assert max_abs(np64(r["o"][ri]), eo) <= TOL_OUT
+    assert max_abs(np64(r["lse"][:, ri]), el) <= TOL_LSE
+    log(f"path {name}: oracle dQ rows")
+    rr, edq, _ = oracle.attn_bwd_dq_rows(qf, k64, v64, dof, pos_o, rows)
+    assert max_abs(np64(r["dq"][torch.from_numpy(rr).to("cuda:0")]), edq) <= TOL_OUT
+    log(f"path {name}: oracle dK/dV rows")
+    _, end = oracle.doc_bounds(pos)
+    ends = np.unique(end)[:3]
+    kv_rows = np.unique(np.concatenate([np.arange(max(0, e - 31), e + 1) for e in ends]))
+    rr, edk, edv = oracle.attn_bwd_dkdv_rows(qf, k64, v64, dof, pos_o, kv_rows)
+    ri = torch.from_numpy(rr).to("cuda:0")
+    assert max_abs(np64(r["dk"][ri]), edk) <= TOL_OUT
+    assert max_abs(np64(r["dv"][ri]), edv) <= TOL_OUT
+    # per-document sums of dK and dV over the whole tensor
+    dk64, dv64 = np64(r["dk"]), np64(r["dv"])
+    do_sum = r["do"].double().reshape(N, r["k"].shape[1], -1, r["D"]).sum(dim=2)
+    start, _ = oracle.doc_bounds(pos)
+    for s in np.unique(start)[:8]:
+        e = int(end[s]) + 1
+        L = e - s
+        assert np.abs(dk64[s:e].sum(axis=0)).max() <= TOL_OUT * np.sqrt(L)
+        assert np.abs(dv64[s:e].sum(axis=0) - np64(do_sum[s:e].sum(dim=0))).max() <= TOL_OUT * np.sqrt(L)
+
+
+@pytest.mark.timeout(300)
+def test_million_zero_queries_closed_forms():
+    """Q = 0 over one 1M-token document: O_i = mean(V[0..i]), LSE_i = ln(i+1), dK = 0,
+    dV_j = sum_{i>=j} (sum over the group of dO_i) / (i+1)."""
+    require_gpu()
+    log("path million Q=0")
+    r = _run("million", zero_q=True)
+    N, D = r["N"], r["D"]
+    v = r["v"].double()[:, 0]
+    idx = torch.arange(1, N + 1, device="cuda:0", dtype=torch.float64)
+    mean = torch.cumsum(v, dim=0) / idx[:, None]
+    for h in range(r["q"].shape[1]):
+        assert float((r["o"][:, h].double() - mean).abs().max()) <= TOL_OUT
+        assert float((r["lse"][h].double() - torch.log(idx)).abs().max()) <= TOL_LSE
+    assert float(r["dk"].abs().max()) <= TOL_OUT
+    g = r["do"].double().sum(dim=1) / idx[:, None]          # group sum of dO_i / (i+1)
+    dv_ref = torch.flip(torch.cumsum(torch.flip(g, [0]), dim=0), [0])
+    assert float((r["dv"][:, 0].double() - dv_ref).abs().max()) <= TOL_OUT
+
+
+@pytest.mark.timeout(300)
+def test_training_share_deterministic():
+    require_gpu()
+    a = _run("train_packed")
+    b = _run("train_packed")
+    for name in ("o", "lse", "dq", "dk", "dv", "o_seq", "dq_seq"):
+        assert torch.equal(a[name], b[name]), name

@@ -26,6 +26,9 @@ __all__ = [
     "attn_workspace_bytes",
     "attn_fwd",
     "attn_bwd",
+    "timing_enable",
+    "timing_reset",
+    "timing_read",
     "UL_OK",
     "UL_ERR_ARG",
     "UL_ERR_UNSUPPORTED",
@@ -56,9 +59,39 @@ SIGNATURES = {
     "ul_attn_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32]),
     "ul_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
     "ul_attn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
+    "ul_timing_enable": (_I32, [_I32]),
+    "ul_timing_reset": (None, []),
+    "ul_timing_read": (_I32, [_I32, ctypes.c_char_p, _SZ, ctypes.POINTER(ctypes.c_double),
+                              ctypes.POINTER(ctypes.c_int64)]),
     "ul_last_error": (ctypes.c_char_p, []),
     "ul_version": (ctypes.c_char_p, []),
 }
+
+
+def timing_enable(on=True):
+    """Bracket every library kernel with hipEvents on its stream; returns the previous state."""
+    return bool(load().ul_timing_enable(1 if on else 0))
+
+
+def timing_reset():
+    load().ul_timing_reset()
+
+
+def timing_read():
+    """{kernel name: (total milliseconds, launches)} accumulated since the last reset."""
+    lib = load()
+    n = lib.ul_timing_read(-1, None, 0, None, None)
+    if n < 0:
+        raise UlError(UL_ERR_HIP, "timing read failed")
+    out = {}
+    buf = ctypes.create_string_buffer(128)
+    ms = ctypes.c_double()
+    cnt = ctypes.c_int64()
+    for i in range(n):
+        if lib.ul_timing_read(i, buf, 128, ctypes.byref(ms), ctypes.byref(cnt)) < 0:
+            raise UlError(UL_ERR_HIP, "timing read failed")
+        out[buf.value.decode()] = (ms.value, cnt.value)
+    return out
 
 
 class UlError(RuntimeError):

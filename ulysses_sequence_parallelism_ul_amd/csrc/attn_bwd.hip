@@ -1,8 +1,529 @@
+// Step 2 backward, bf16 inputs, on gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
+//
+// The pages describe no backward; this is the chain rule of the forward
+// (page "Hugging Face并行加速", nmedialink.com, section "Ulysses的工作原理",
+// step 4) with P recomputed from the saved log-sum-exp, which keeps memory
+// linear in N as the tiled forward does (same page, section
+// "超长序列训练的挑战"):
+//   delta_c = sum_d dO_c O_c,   P = exp(scale Q K^T - lse),   dP = dO V^T,
+//   dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// Query columns interleave the G query heads of a KV head (column
+// c = token * G + head_in_group), so dK and dV sum over the group for free.
+//
+// Three kernels, no atomics (bitwise deterministic):
+//  * delta_bf16_kernel: delta per query column (fp32).
+//  * dkdv_kernel (key-outer): a wave owns 32 keys with K and V in registers
+//    and accumulates dK^T and dV^T over every query tile that can see its
+//    keys.  Scores are formed as S = Q K^T (columns x keys) so that P and dS
+//    come out of the MFMA already shaped as the B operand of dV^T += dO^T P
+//    and dK^T += Q^T dS; Q and dO tiles are staged row-major (rows permuted so
+//    each accumulator group covers 8 consecutive columns) and their transposes
+//    come from blocked copies made by one pre-pass.
+//  * dq_kernel (query-outer, like the forward): a wave owns 32 query columns
+//    with Q and dO in registers; S^T and dP^T are recomputed per key tile and
+//    dQ^T += K^T dS^T uses a blocked K^T copy.
+// Tiles outside the causal band and outside the documents are never visited;
+// tiles that are fully visible skip the per-element mask.
 #include "ul_internal.h"
+
+#include <math.h>
+
 namespace ul {
-hipError_t launch_attn_bwd_bf16(const bf16*, const bf16*, const bf16*, const bf16*, const bf16*, const float*,
-                                const int32_t*, const int32_t*, float*, float*, float*, float*, bf16*, bf16*, bf16*,
-                                int, int, int, int, float, hipStream_t) {
-  return hipErrorNotSupported;
+
+hipError_t launch_transpose_blocked(const bf16* src, bf16* dst, int64_t ncols, int H, int Hkv, int lgG, int D,
+                                    hipStream_t s);
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int perm_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)s[base + e];
+  return r;
 }
+
+__device__ __forceinline__ int64_t col_offset(int64_t c, int lgG, int Hkv, int hk, int D) {
+  // element offset of query column c of KV group hk in a [N][Hq][D] tensor
+  return ((((c >> lgG) * Hkv + hk) << lgG) + (c & ((1 << lgG) - 1))) * D;
+}
+
+// ------------------------------------------------------------------ delta --
+template <int D>
+__global__ void __launch_bounds__(256) delta_bf16_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
+                                                       float* __restrict__ delta, int64_t NG, int Hkv, int lgG) {
+  constexpr int LPC = D / 8;        // lanes per column (8 elements each)
+  constexpr int CPB = 256 / LPC;    // columns per block
+  const int hk = blockIdx.y;
+  const int64_t c = (int64_t)blockIdx.x * CPB + threadIdx.x / LPC;
+  const int part = threadIdx.x % LPC;
+  float s = 0.0f;
+  if (c < NG) {
+    const int64_t off = col_offset(c, lgG, Hkv, hk, D) + part * 8;
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + off);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)a[e], (float)b[e], s);
+  }
+#pragma unroll
+  for (int m = LPC / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (c < NG && part == 0) delta[(int64_t)hk * NG + c] = s;
+}
+
+// ------------------------------------------------------------------- dK dV --
+template <int D, int NW>
+struct DkvCfg {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int BNK = NW * 32;      // keys per work-group
+  static constexpr int BQ = 64;            // query columns per tile
+  static constexpr int RSTR = D * 2 + 16;  // LDS bytes per Q / dO row
+  static constexpr int TSTR = BQ * 2 + 16; // LDS bytes per Q^T / dO^T row
+  static constexpr int RBYTES = BQ * RSTR;
+  static constexpr int TBYTES = D * TSTR;
+  static constexpr int AUX = BQ * 4 * 4;   // lse2, delta, row, doc start per column
+  static constexpr int Q_OFF = 0, DO_OFF = RBYTES, QT_OFF = 2 * RBYTES, DOT_OFF = 2 * RBYTES + TBYTES,
+                       AUX_OFF = 2 * RBYTES + 2 * TBYTES;
+  static constexpr int SMEM = AUX_OFF + AUX;
+  static constexpr int RCH = BQ * D / 8;   // 16-byte chunks per row tile
+  static constexpr int TCH = D * BQ / 8;   // 16-byte chunks per transposed tile
+  static constexpr int RPT = RCH / kThreads;
+  static constexpr int TPT = TCH / kThreads;
+  static_assert(RCH % kThreads == 0 && TCH % kThreads == 0, "tile chunks must split evenly");
+  static_assert(kThreads >= BQ, "aux load needs one thread per column");
+};
+
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64) dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const bf16* __restrict__ qt, const bf16* __restrict__ dot, const int32_t* __restrict__ doc_start,
+    const int32_t* __restrict__ doc_end, float* __restrict__ dk, float* __restrict__ dv, int N, int Hkv, int lgG,
+    float sl2, float scale, int nkb, int ncb) {
+  using C = DkvCfg<D, NW>;
+  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
+  const int G = 1 << lgG;
+  const int hk = blockIdx.x % Hkv;
+  const int kblk = (int)(blockIdx.x / Hkv);  // block 0 sees the most queries: launched first
+  const int64_t NG = (int64_t)N << lgG;
+  const int kb0 = kblk * C::BNK;
+  const int kb_last = min(N - 1, kb0 + C::BNK - 1);
+  const int row_end = doc_end[kb_last];
+  const int tq_lo = (int)(((int64_t)kb0 << lgG) / C::BQ);
+  const int tq_hi = (int)((((int64_t)(row_end + 1) << lgG) - 1) / C::BQ);
+
+  // this lane's key
+  const int key = kb0 + w * 32 + lc;
+  const bool kvalid = key < N;
+  bf16x8 kreg[D / 16], vreg[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if (kvalid) {
+      const int64_t off = ((int64_t)key * Hkv + hk) * D + ks * 16 + g * 8;
+      kreg[ks] = *reinterpret_cast<const bf16x8*>(k + off);
+      vreg[ks] = *reinterpret_cast<const bf16x8*>(v + off);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { kreg[ks][e] = (bf16)0.0f; vreg[ks][e] = (bf16)0.0f; }
+    }
+  }
+  f32x16 dkt[D / 32], dvt[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { dkt[db][i] = 0.0f; dvt[db][i] = 0.0f; }
+
+  u32x4 rq[C::RPT], rdo[C::RPT], rqt[C::TPT], rdot[C::TPT];
+  float a_lse = 0.0f, a_dl = 0.0f;
+  int a_row = -1, a_ds = 0;
+  auto gload = [&](int tq) {
+    const int64_t tc0 = (int64_t)tq * C::BQ;
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) {
+      const int ch = tid + i * C::kThreads;
+      const int r = ch / (D / 8), part = ch % (D / 8);
+      const int64_t c = tc0 + r;
+      if (c < NG) {
+        const int64_t off = col_offset(c, lgG, Hkv, hk, D) + part * 8;
+        rq[i] = *reinterpret_cast<const u32x4*>(q + off);
+        rdo[i] = *reinterpret_cast<const u32x4*>(dout + off);
+      } else {
+        rq[i] = u32x4{0u, 0u, 0u, 0u};
+        rdo[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    const int64_t tb = ((int64_t)hk * ncb + tq) * (int64_t)(D * C::BQ);
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+      const int ch = tid + i * C::kThreads;
+      rqt[i] = *reinterpret_cast<const u32x4*>(qt + tb + ch * 8);
+      rdot[i] = *reinterpret_cast<const u32x4*>(dot + tb + ch * 8);
+    }
+    if (tid < C::BQ) {
+      const int64_t c = tc0 + tid;
+      if (c < NG) {
+        const int row = (int)(c >> lgG);
+        const int h = (hk << lgG) + (int)(c & (G - 1));
+        a_lse = lse[(int64_t)h * N + row] * kLog2e;
+        a_dl = delta[(int64_t)hk * NG + c];
+        a_row = row;
+        a_ds = doc_start[row];
+      } else {
+        a_lse = 0.0f;
+        a_dl = 0.0f;
+        a_row = -1;
+        a_ds = 0;
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) {
+      const int ch = tid + i * C::kThreads;
+      const int r = ch / (D / 8), part = ch % (D / 8);
+      const int rp = (r & 32) | perm_row(r & 31);
+      *reinterpret_cast<u32x4*>(smem + C::Q_OFF + rp * C::RSTR + part * 16) = rq[i];
+      *reinterpret_cast<u32x4*>(smem + C::DO_OFF + rp * C::RSTR + part * 16) = rdo[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+      const int ch = tid + i * C::kThreads;
+      const int d = ch / (C::BQ / 8), part = ch % (C::BQ / 8);
+      *reinterpret_cast<u32x4*>(smem + C::QT_OFF + d * C::TSTR + part * 16) = rqt[i];
+      *reinterpret_cast<u32x4*>(smem + C::DOT_OFF + d * C::TSTR + part * 16) = rdot[i];
+    }
+    if (tid < C::BQ) {
+      float* af = reinterpret_cast<float*>(smem + C::AUX_OFF);
+      int* ai = reinterpret_cast<int*>(smem + C::AUX_OFF);
+      af[tid] = a_lse;
+      af[C::BQ + tid] = a_dl;
+      ai[2 * C::BQ + tid] = a_row;
+      ai[3 * C::BQ + tid] = a_ds;
+    }
+  };
+
+  gload(tq_lo);
+  lstore();
+  __syncthreads();
+  const float* aux_lse = reinterpret_cast<const float*>(smem + C::AUX_OFF);
+  const float* aux_dl = aux_lse + C::BQ;
+  const int* aux_row = reinterpret_cast<const int*>(smem + C::AUX_OFF) + 2 * C::BQ;
+  const int* aux_ds = aux_row + C::BQ;
+  for (int tq = tq_lo; tq <= tq_hi; ++tq) {
+    if (tq < tq_hi) gload(tq + 1);
+    const int64_t tc0 = (int64_t)tq * C::BQ;
+    const int first_row = (int)(tc0 >> lgG);
+    const int last_row = (int)(min<int64_t>(NG - 1, tc0 + C::BQ - 1) >> lgG);
+    const bool need_mask = first_row < kb_last || doc_start[last_row] > kb0 || tc0 + C::BQ > NG;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { s[i] = 0.0f; dp[i] = 0.0f; }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(smem + C::Q_OFF + (qh * 32 + lc) * C::RSTR + ks * 32 + g * 16);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s, 0, 0, 0);
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(smem + C::DO_OFF + (qh * 32 + lc) * C::RSTR + ks * 32 + g * 16);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dp, 0, 0, 0);
+      }
+      // register i holds query column qh*32 + (i>>3)*16 + g*8 + (i&7) of the tile
+      f32x16 pr, dsr;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int cb = qh * 32 + half * 16 + g * 8;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(aux_lse + cb);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(aux_lse + cb + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(aux_dl + cb);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(aux_dl + cb + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = half * 8 + e;
+          const float lv = e < 4 ? l0[e] : l1[e - 4];
+          const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -lv));
+          if (need_mask) {
+            const int row = aux_row[cb + e];
+            if (!(key <= row && key >= aux_ds[cb + e])) p = 0.0f;
+          }
+          pr[i] = p;
+          dsr[i] = p * (dp[i] - dv_);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 bp = pack8(pr, kk * 8);
+        const bf16x8 bs = pack8(dsr, kk * 8);
+        const int qoff = (qh * 32 + kk * 16 + g * 8) * 2;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 adot = *reinterpret_cast<const bf16x8*>(smem + C::DOT_OFF + (db * 32 + lc) * C::TSTR + qoff);
+          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adot, bp, dvt[db], 0, 0, 0);
+          const bf16x8 aqt = *reinterpret_cast<const bf16x8*>(smem + C::QT_OFF + (db * 32 + lc) * C::TSTR + qoff);
+          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, bs, dkt[db], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    if (tq < tq_hi) {
+      lstore();
+    }
+    __syncthreads();
+  }
+
+  if (kvalid) {
+    const int64_t base = ((int64_t)key * Hkv + hk) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + j * 8 + g * 4;
+        f32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = dkt[db][j * 4 + e] * scale;
+          b[e] = dvt[db][j * 4 + e];
+        }
+        *reinterpret_cast<f32x4*>(dk + base + d) = a;
+        *reinterpret_cast<f32x4*>(dv + base + d) = b;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------- dQ --
+template <int D, int NW>
+struct DqCfg {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int BN = 64;            // keys per tile
+  static constexpr int BMC = NW * 32;      // query columns per work-group
+  static constexpr int RSTR = D * 2 + 16;  // LDS bytes per K / V row
+  static constexpr int TSTR = BN * 2 + 16; // LDS bytes per K^T row
+  static constexpr int RBYTES = BN * RSTR;
+  static constexpr int TBYTES = D * TSTR;
+  static constexpr int K_OFF = 0, V_OFF = RBYTES, KT_OFF = 2 * RBYTES;
+  static constexpr int STAGE = 2 * RBYTES + TBYTES;
+  static constexpr int RCH = BN * D / 8;
+  static constexpr int TCH = D * BN / 8;
+  static constexpr int RPT = RCH / kThreads;
+  static constexpr int TPT = TCH / kThreads;
+  static_assert(RCH % kThreads == 0 && TCH % kThreads == 0, "tile chunks must split evenly");
+};
+
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64) dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const bf16* __restrict__ kt, const int32_t* __restrict__ doc_start, float* __restrict__ dq, int N, int Hkv,
+    int lgG, float sl2, float scale, int ncb, int nb) {
+  using C = DqCfg<D, NW>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
+  const int G = 1 << lgG;
+  const int hk = blockIdx.x % Hkv;
+  const int cb = ncb - 1 - (int)(blockIdx.x / Hkv);  // heaviest column blocks first
+  const int64_t NG = (int64_t)N << lgG;
+  const int64_t c0 = (int64_t)cb * C::BMC;
+  const int r_first = (int)(c0 >> lgG);
+  const int r_last = (int)min<int64_t>(N - 1, (c0 + C::BMC - 1) >> lgG);
+  const int t_lo = doc_start[r_first] / C::BN;
+  const int t_hi = r_last / C::BN;
+  const int ds_last = doc_start[r_last];
+
+  const int64_t c = c0 + w * 32 + lc;
+  const bool cvalid = c < NG;
+  const int row = cvalid ? (int)(c >> lgG) : -1;
+  const int ds_c = cvalid ? doc_start[row] : 0;
+  const int64_t qoff = cvalid ? col_offset(c, lgG, Hkv, hk, D) : 0;
+  float lse2 = 0.0f, dl = 0.0f;
+  bf16x8 qreg[D / 16], doreg[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if (cvalid) {
+      qreg[ks] = *reinterpret_cast<const bf16x8*>(q + qoff + ks * 16 + g * 8);
+      doreg[ks] = *reinterpret_cast<const bf16x8*>(dout + qoff + ks * 16 + g * 8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { qreg[ks][e] = (bf16)0.0f; doreg[ks][e] = (bf16)0.0f; }
+    }
+  }
+  if (cvalid) {
+    const int h = (hk << lgG) + (int)(c & (G - 1));
+    lse2 = lse[(int64_t)h * N + row] * kLog2e;
+    dl = delta[(int64_t)hk * NG + c];
+  }
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+
+  u32x4 rk[C::RPT], rv[C::RPT], rkt[C::TPT];
+  auto gload = [&](int t) {
+    const int t0 = t * C::BN;
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) {
+      const int ch = tid + i * C::kThreads;
+      const int r = ch / (D / 8), part = ch % (D / 8);
+      const int kv = t0 + r;
+      if (kv < N) {
+        const int64_t off = ((int64_t)kv * Hkv + hk) * D + part * 8;
+        rk[i] = *reinterpret_cast<const u32x4*>(k + off);
+        rv[i] = *reinterpret_cast<const u32x4*>(v + off);
+      } else {
+        rk[i] = u32x4{0u, 0u, 0u, 0u};
+        rv[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    const bf16* src = kt + ((int64_t)hk * nb + t) * (int64_t)(D * C::BN);
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+      const int ch = tid + i * C::kThreads;
+      rkt[i] = *reinterpret_cast<const u32x4*>(src + ch * 8);
+    }
+  };
+  auto lstore = [&](int st) {
+    char* b = smem + st * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) {
+      const int ch = tid + i * C::kThreads;
+      const int r = ch / (D / 8), part = ch % (D / 8);
+      const int rp = (r & 32) | perm_row(r & 31);
+      *reinterpret_cast<u32x4*>(b + C::K_OFF + rp * C::RSTR + part * 16) = rk[i];
+      *reinterpret_cast<u32x4*>(b + C::V_OFF + rp * C::RSTR + part * 16) = rv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+      const int ch = tid + i * C::kThreads;
+      const int d = ch / (C::BN / 8), part = ch % (C::BN / 8);
+      *reinterpret_cast<u32x4*>(b + C::KT_OFF + d * C::TSTR + part * 16) = rkt[i];
+    }
+  };
+
+  gload(t_lo);
+  lstore(0);
+  __syncthreads();
+  for (int t = t_lo; t <= t_hi; ++t) {
+    const int st = (t - t_lo) & 1;
+    if (t < t_hi) gload(t + 1);
+    const char* b = smem + st * C::STAGE;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { s[kb][i] = 0.0f; dp[kb][i] = 0.0f; }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(b + C::K_OFF + (kb * 32 + lc) * C::RSTR + ks * 32 + g * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], s[kb], 0, 0, 0);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(b + C::V_OFF + (kb * 32 + lc) * C::RSTR + ks * 32 + g * 16);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[ks], dp[kb], 0, 0, 0);
+      }
+    }
+    const int t0 = t * C::BN;
+    const bool need_mask = t0 + C::BN - 1 > r_first || t0 < ds_last;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], sl2, -lse2));
+        if (need_mask) {
+          const int kv = t0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+          if (!(kv <= row && kv >= ds_c)) p = 0.0f;
+        }
+        s[kb][i] = p * (dp[kb][i] - dl);  // dS^T
+      }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bf16x8 bs = pack8(s[tt >> 1], (tt & 1) * 8);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(b + C::KT_OFF + (db * 32 + lc) * C::TSTR + tt * 32 + g * 16);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, acc[db], 0, 0, 0);
+      }
+    }
+    if (t < t_hi) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  if (cvalid) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = acc[db][j * 4 + e] * scale;
+        *reinterpret_cast<f32x4*>(dq + qoff + db * 32 + j * 8 + g * 4) = a;
+      }
+  }
+}
+
+int ilog2_pow2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o, const bf16* dout,
+                                const float* lse, const int32_t* doc_start, const int32_t* doc_end, float* dq,
+                                float* dk, float* dv, float* delta, bf16* qt, bf16* dot, bf16* kt, int N, int Hq,
+                                int Hkv, int D, float scale, hipStream_t s) {
+  const int G = Hq / Hkv;
+  const int lgG = ilog2_pow2(G);
+  const int64_t NG = (int64_t)N * G;
+  const float sl2 = scale * kLog2e;
+  // pre-passes: delta, blocked transposes of Q, dO (query columns) and K (keys)
+  {
+    const int cpb = 256 / (D / 8);
+    const dim3 grid((unsigned)((NG + cpb - 1) / cpb), Hkv);
+    TimedLaunch timer("attn_bwd_delta", s);
+    if (D == 128)
+      hipLaunchKernelGGL(delta_bf16_kernel<128>, grid, dim3(256), 0, s, o, dout, delta, NG, Hkv, lgG);
+    else
+      hipLaunchKernelGGL(delta_bf16_kernel<64>, grid, dim3(256), 0, s, o, dout, delta, NG, Hkv, lgG);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch_transpose_blocked(q, qt, NG, Hq, Hkv, lgG, D, s);
+  if (e != hipSuccess) return e;
+  e = launch_transpose_blocked(dout, dot, NG, Hq, Hkv, lgG, D, s);
+  if (e != hipSuccess) return e;
+  e = launch_transpose_blocked(k, kt, N, Hkv, Hkv, 0, D, s);
+  if (e != hipSuccess) return e;
+  const int ncb_t = (int)((NG + kTB - 1) / kTB);  // blocked column tiles of the transposed copies
+  const int nb = (N + kTB - 1) / kTB;
+  {
+    constexpr int NW = 4;
+    const int nkb = (N + NW * 32 - 1) / (NW * 32);
+    const dim3 grid((unsigned)((int64_t)nkb * Hkv)), block(NW * 64);
+    TimedLaunch timer("attn_bwd_dkdv", s);
+    if (D == 128)
+      hipLaunchKernelGGL((dkdv_kernel<128, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, qt, dot, doc_start,
+                         doc_end, dk, dv, N, Hkv, lgG, sl2, scale, nkb, ncb_t);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<64, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, qt, dot, doc_start,
+                         doc_end, dk, dv, N, Hkv, lgG, sl2, scale, nkb, ncb_t);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    constexpr int NW = 8;
+    const int ncb = (int)((NG + NW * 32 - 1) / (NW * 32));
+    const dim3 grid((unsigned)((int64_t)ncb * Hkv)), block(NW * 64);
+    TimedLaunch timer("attn_bwd_dq", s);
+    if (D == 128)
+      hipLaunchKernelGGL((dq_kernel<128, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, kt, doc_start, dq, N,
+                         Hkv, lgG, sl2, scale, ncb, nb);
+    else
+      hipLaunchKernelGGL((dq_kernel<64, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, kt, doc_start, dq, N,
+                         Hkv, lgG, sl2, scale, ncb, nb);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace ul

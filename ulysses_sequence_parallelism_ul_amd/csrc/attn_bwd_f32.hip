@@ -102,6 +102,7 @@ hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, c
                                float* dk, float* dv, float* delta, int N, int Hq, int Hkv, int D, float scale,
                                hipStream_t s) {
   const dim3 gq((unsigned)(((int64_t)N * Hq + 63) / 64)), gk((unsigned)(((int64_t)N * Hkv + 63) / 64)), b(64);
+  TimedLaunch timer("attn_bwd_f32", s);
   if (D == 128) {
     hipLaunchKernelGGL(delta_f32_kernel<128>, gq, b, 0, s, o, dout, delta, N, Hq);
     hipLaunchKernelGGL(dq_f32_kernel<128>, gq, b, 0, s, q, k, v, dout, lse, delta, doc_start, dq, N, Hq, Hkv, scale);

@@ -304,6 +304,7 @@ hipError_t launch_attn_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, con
   const int64_t ncols = (int64_t)N * (Hq / Hkv);
   const int ncb = (int)((ncols + NW * 32 - 1) / (NW * 32));
   const dim3 grid((unsigned)((int64_t)ncb * Hkv)), block(NW * 64);
+  TimedLaunch timer("attn_fwd_bf16", s);
   if (D == 128)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, NW>), grid, block, 0, s, q, k, vt_ws, doc_start, o, lse, N, Hkv,
                        lgG, sl2, ncb, nb);
@@ -318,6 +319,7 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, c
   const int64_t ncols = (int64_t)N * Hq;
   const dim3 grid((unsigned)((ncols + 63) / 64)), block(64);
   const float sl2 = scale * kLog2e;
+  TimedLaunch timer("attn_fwd_f32", s);
   if (D == 128)
     hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, block, 0, s, q, k, v, doc_start, o, lse, N, Hq, Hkv, sl2);
   else

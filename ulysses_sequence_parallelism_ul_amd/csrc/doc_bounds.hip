@@ -123,6 +123,7 @@ __global__ void __launch_bounds__(kThreads) docb_scan(const int32_t* __restrict_
 hipError_t launch_doc_bounds(const int32_t* pos, int32_t* doc_start, int32_t* doc_end, int32_t* scan, int N,
                              hipStream_t s) {
   const int nblk = (N + kScanBlock - 1) / kScanBlock;
+  TimedLaunch timer("doc_bounds", s);
   hipLaunchKernelGGL(docb_reduce, dim3(nblk), dim3(kThreads), 0, s, pos, scan, N, nblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -71,6 +71,7 @@ hipError_t launch_t(const void* src, void* dst, int64_t N, int64_t run_bytes, in
   const int64_t per_block = (int64_t)kThreads * kUnroll;
   const int64_t blocks = (total + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  TimedLaunch timer(s2h ? "relayout_seq_to_head" : "relayout_head_to_seq", s);
   hipLaunchKernelGGL(relayout_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                      static_cast<const T*>(src), static_cast<T*>(dst), total, run, ilog2_exact(run),
                      row_bytes / (int64_t)sizeof(T), off_bytes / (int64_t)sizeof(T), s2h ? 1 : 0);

@@ -53,6 +53,7 @@ hipError_t launch_transpose_blocked(const bf16* src, bf16* dst, int64_t ncols, i
                                     hipStream_t s) {
   const int nblk = (int)((ncols + kTB - 1) / kTB);
   dim3 grid(nblk, Hkv);
+  TimedLaunch timer("transpose_blocked", s);
   if (D == 128)
     hipLaunchKernelGGL(transpose_blocked_kernel<128>, grid, dim3(256), 0, s, src, dst, ncols, H, lgG, nblk);
   else if (D == 64)

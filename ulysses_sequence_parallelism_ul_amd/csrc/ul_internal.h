@@ -40,6 +40,22 @@ struct WsLayout {
 
 WsLayout ws_layout(int64_t N, int Hq, int Hkv, int D, ul_dtype dt, bool for_bwd);
 
+// Optional per-kernel timing (ul_timing_enable): when on, launchers bracket
+// each kernel with hipEvents recorded on the kernel's own stream.
+bool timing_on();
+void timing_begin(const char* name, hipStream_t s);
+void timing_end(hipStream_t s);
+struct TimedLaunch {
+  hipStream_t s;
+  bool on;
+  TimedLaunch(const char* name, hipStream_t st) : s(st), on(timing_on()) {
+    if (on) timing_begin(name, s);
+  }
+  ~TimedLaunch() {
+    if (on) timing_end(s);
+  }
+};
+
 // ---- launchers (enqueue only; arguments already validated) ----
 hipError_t launch_relayout(const void* src, void* dst, int64_t N, int H, int D, int P, int rank,
                            int elem_bytes, bool seq_to_head, hipStream_t s);
