@@ -99,10 +99,8 @@ namespace ul {
 WsLayout ws_layout(int64_t N, int Hq, int Hkv, int D, ul_dtype dt, bool for_bwd) {
   WsLayout L;
   const size_t A = 256;
-  const int64_t G = Hq / Hkv;
   const int64_t nblk = (N + kScanBlock - 1) / kScanBlock;
   const int64_t NB = (N + kTB - 1) / kTB;
-  const int64_t CB = (N * G + kTB - 1) / kTB;
   size_t off = 0;
   L.doc_start = off; off = align_up(off + (size_t)N * 4, A);
   L.doc_end = off;   off = align_up(off + (size_t)N * 4, A);
@@ -112,11 +110,6 @@ WsLayout ws_layout(int64_t N, int Hq, int Hkv, int D, ul_dtype dt, bool for_bwd)
   }
   if (for_bwd) {
     L.delta = off; off = align_up(off + (size_t)Hq * N * 4, A);
-    if (dt == UL_BF16) {
-      L.qt = off;  off = align_up(off + (size_t)Hkv * CB * D * kTB * 2, A);
-      L.dot = off; off = align_up(off + (size_t)Hkv * CB * D * kTB * 2, A);
-      L.kt = off;  off = align_up(off + (size_t)Hkv * NB * D * kTB * 2, A);
-    }
   }
   L.total = off;
   return L;
@@ -247,8 +240,7 @@ ul_status ul_attn_bwd(const void* q, const void* k, const void* v, const void* o
     err = ul::launch_attn_bwd_bf16(
         static_cast<const ul::bf16*>(q), static_cast<const ul::bf16*>(k), static_cast<const ul::bf16*>(v),
         static_cast<const ul::bf16*>(o), static_cast<const ul::bf16*>(dout), lse, ds, de, dq, dk, dv, delta,
-        reinterpret_cast<ul::bf16*>(w + L.qt), reinterpret_cast<ul::bf16*>(w + L.dot),
-        reinterpret_cast<ul::bf16*>(w + L.kt), (int)N, Hq, Hkv, D, scale, s);
+        (int)N, Hq, Hkv, D, scale, s);
   else
     err = ul::launch_attn_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                   static_cast<const float*>(v), static_cast<const float*>(o),

@@ -12,16 +12,20 @@
 //
 // Three kernels, no atomics (bitwise deterministic):
 //  * delta_bf16_kernel: delta per query column (fp32).
-//  * dkdv_kernel (key-outer): a wave owns 32 keys with K and V in registers
-//    and accumulates dK^T and dV^T over every query tile that can see its
-//    keys.  Scores are formed as S = Q K^T (columns x keys) so that P and dS
-//    come out of the MFMA already shaped as the B operand of dV^T += dO^T P
-//    and dK^T += Q^T dS; Q and dO tiles are staged row-major (rows permuted so
-//    each accumulator group covers 8 consecutive columns) and their transposes
-//    come from blocked copies made by one pre-pass.
+//  * dkdv_kernel (key-outer): a work-group owns 128 keys, whose K and V rows
+//    stay in LDS; its 8 waves (two per SIMD) pair up on 32-key blocks and
+//    split every query tile into halves, accumulating dK^T and dV^T in
+//    registers over every query tile that can see their keys.  Scores are
+//    formed as S = Q K^T (columns x keys) so that P and dS come out of the MFMA
+//    already shaped as the B operand of dV^T += dO^T P and dK^T += Q^T dS.  Q
+//    and dO tiles are staged row-major in LDS (rows permuted so each
+//    accumulator group covers 8 consecutive columns, 16-byte chunks XOR
+//    swizzled against bank conflicts); the transposed A operands dO^T and Q^T
+//    are read from the same tiles with the gfx950 LDS transpose read
+//    (ds_read_b64_tr_b16), so only 32 KiB per 64-column tile crosses from L2.
 //  * dq_kernel (query-outer, like the forward): a wave owns 32 query columns
 //    with Q and dO in registers; S^T and dP^T are recomputed per key tile and
-//    dQ^T += K^T dS^T uses a blocked K^T copy.
+//    dQ^T += K^T dS^T takes K^T from the K tile by transpose reads.
 // Tiles outside the causal band and outside the documents are never visited;
 // tiles that are fully visible skip the per-element mask.
 #include "ul_internal.h"
@@ -30,14 +34,28 @@
 
 namespace ul {
 
-hipError_t launch_transpose_blocked(const bf16* src, bf16* dst, int64_t ncols, int H, int Hkv, int lgG, int D,
-                                    hipStream_t s);
-
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int perm_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+// LDS row of tile row r (0..63): permuted within each half of 32
+__device__ __forceinline__ int tile_row(int r) { return (r & 32) | perm_row(r & 31); }
+
+// Byte offset of 16-byte chunk `chunk` of physical row `prow` in an unpadded
+// [64][D] bf16 LDS tile whose chunks are XOR-swizzled per row (chunk c of row
+// r sits in slot c ^ swz(r)).  The swizzle keeps both access patterns used
+// here free of bank conflicts: 16 consecutive rows read at the same chunk
+// (MFMA row operands), and 4 consecutive rows x 4 consecutive chunks read by
+// 32 lanes (transpose reads).
+template <int D>
+__device__ __forceinline__ int lds_off(int prow, int chunk) {
+  constexpr int CPR = D / 8;
+  const int swz = (((prow & 3) << 2) ^ ((prow >> 2) & 3)) & (CPR - 1);
+  return prow * (D * 2) + ((chunk ^ swz) << 4);
+}
 
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   bf16x8 r;
@@ -49,6 +67,28 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
 __device__ __forceinline__ int64_t col_offset(int64_t c, int lgG, int Hkv, int hk, int D) {
   // element offset of query column c of KV group hk in a [N][Hq][D] tensor
   return ((((c >> lgG) * Hkv + hk) << lgG) + (c & ((1 << lgG) - 1))) * D;
+}
+
+// A operand of a 32x32x16 MFMA whose rows are the feature axis of a row-major
+// [64 rows][D] bf16 LDS tile (rows stored at tile_row(), chunks swizzled) and
+// whose k axis is the tile's row axis: lane l gets feature d0 + (l & 31) of
+// rows k0 + 8*(l >> 5) + 0..7.  Within each 16-lane group the transpose read
+// hands lane j element (j & 3) of the 8-byte chunks read by lanes
+// (j >> 2) + 4e, e = 0..3, so lane s reads row k + (s >> 2), features
+// n0 + 4*(s & 3) .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr_a(const char* tile, int d0, int k0, int lane) {
+  const int m = lane >> 4, s = lane & 15;
+  const int n = d0 + (m & 1) * 16 + 4 * (s & 3);
+  const int k = k0 + (m >> 1) * 8 + (s >> 2);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const lds_s16x4* p1 = (const lds_s16x4*)(tile + lds_off<D>(tile_row(k), n >> 3) + (n & 7) * 2);
+  const lds_s16x4* p2 = (const lds_s16x4*)(tile + lds_off<D>(tile_row(k + 4), n >> 3) + (n & 7) * 2);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p2);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // ------------------------------------------------------------------ delta --
@@ -74,37 +114,46 @@ __global__ void __launch_bounds__(256) delta_bf16_kernel(const bf16* __restrict_
 }
 
 // ------------------------------------------------------------------- dK dV --
-template <int D, int NW>
+// A work-group owns 128 keys of one KV head; their K and V rows sit in LDS
+// for the whole kernel.  Eight waves, two per SIMD: waves w and w+4 share the
+// 32-key block (w & 3) and split every 64-column query tile into halves, each
+// accumulating partial dK^T and dV^T in registers; the halves are summed
+// through LDS at the end.
+template <int D>
 struct DkvCfg {
+  static constexpr int NW = 8;
   static constexpr int kThreads = NW * 64;
-  static constexpr int BNK = NW * 32;      // keys per work-group
+  static constexpr int BNK = 128;          // keys per work-group
   static constexpr int BQ = 64;            // query columns per tile
-  static constexpr int RSTR = D * 2 + 16;  // LDS bytes per Q / dO row
-  static constexpr int TSTR = BQ * 2 + 16; // LDS bytes per Q^T / dO^T row
+  static constexpr int KSTR = D * 2 + 16;  // LDS bytes per K / V row (padded)
+  static constexpr int KVBYTES = BNK * KSTR;
+  static constexpr int RSTR = D * 2;       // LDS bytes per Q / dO row (swizzled, unpadded)
   static constexpr int RBYTES = BQ * RSTR;
-  static constexpr int TBYTES = D * TSTR;
   static constexpr int AUX = BQ * 4 * 4;   // lse2, delta, row, doc start per column
-  static constexpr int Q_OFF = 0, DO_OFF = RBYTES, QT_OFF = 2 * RBYTES, DOT_OFF = 2 * RBYTES + TBYTES,
-                       AUX_OFF = 2 * RBYTES + 2 * TBYTES;
-  static constexpr int SMEM = AUX_OFF + AUX;
+  static constexpr int Q_OFF = 0, DO_OFF = RBYTES, AUX_OFF = 2 * RBYTES;
+  static constexpr int STAGE = AUX_OFF + AUX;
+  static constexpr int K_LDS = 2 * STAGE, V_LDS = 2 * STAGE + KVBYTES;
+  static constexpr int SMEM = 2 * STAGE + 2 * KVBYTES;
   static constexpr int RCH = BQ * D / 8;   // 16-byte chunks per row tile
-  static constexpr int TCH = D * BQ / 8;   // 16-byte chunks per transposed tile
   static constexpr int RPT = RCH / kThreads;
-  static constexpr int TPT = TCH / kThreads;
-  static_assert(RCH % kThreads == 0 && TCH % kThreads == 0, "tile chunks must split evenly");
-  static_assert(kThreads >= BQ, "aux load needs one thread per column");
+  static constexpr int KVCH = BNK * D / 8;
+  static constexpr int KVPT = KVCH / kThreads;
+  static constexpr int RED_BYTES = 4 * 64 * (D / 32) * 16 * 4;  // one accumulator set of the four upper waves
+  static_assert(RCH % kThreads == 0 && KVCH % kThreads == 0, "tile chunks must split evenly");
+  static_assert(RED_BYTES <= SMEM, "reduction buffer must fit in LDS");
 };
 
-template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64) dkdv_kernel(
+template <int D>
+__global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    const bf16* __restrict__ qt, const bf16* __restrict__ dot, const int32_t* __restrict__ doc_start,
-    const int32_t* __restrict__ doc_end, float* __restrict__ dk, float* __restrict__ dv, int N, int Hkv, int lgG,
-    float sl2, float scale, int nkb, int ncb) {
-  using C = DkvCfg<D, NW>;
+    const int32_t* __restrict__ doc_start, const int32_t* __restrict__ doc_end, float* __restrict__ dk,
+    float* __restrict__ dv, int N, int Hkv, int lgG, float sl2, float scale) {
+  using C = DkvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
+  const int kbw = w & 3;   // this wave's 32-key block
+  const int qh = w >> 2;   // this wave's half of every query tile
   const int G = 1 << lgG;
   const int hk = blockIdx.x % Hkv;
   const int kblk = (int)(blockIdx.x / Hkv);  // block 0 sees the most queries: launched first
@@ -114,29 +163,32 @@ __global__ void __launch_bounds__(NW * 64) dkdv_kernel(
   const int row_end = doc_end[kb_last];
   const int tq_lo = (int)(((int64_t)kb0 << lgG) / C::BQ);
   const int tq_hi = (int)((((int64_t)(row_end + 1) << lgG) - 1) / C::BQ);
-
-  // this lane's key
-  const int key = kb0 + w * 32 + lc;
+  const int key = kb0 + kbw * 32 + lc;
   const bool kvalid = key < N;
-  bf16x8 kreg[D / 16], vreg[D / 16];
+
+  // K and V rows of the work-group's keys into LDS (zero past N)
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    if (kvalid) {
-      const int64_t off = ((int64_t)key * Hkv + hk) * D + ks * 16 + g * 8;
-      kreg[ks] = *reinterpret_cast<const bf16x8*>(k + off);
-      vreg[ks] = *reinterpret_cast<const bf16x8*>(v + off);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { kreg[ks][e] = (bf16)0.0f; vreg[ks][e] = (bf16)0.0f; }
+  for (int i = 0; i < C::KVPT; ++i) {
+    const int ch = tid + i * C::kThreads;
+    const int r = ch / (D / 8), part = ch % (D / 8);
+    const int kr = kb0 + r;
+    u32x4 kv4 = {0u, 0u, 0u, 0u}, vv4 = {0u, 0u, 0u, 0u};
+    if (kr < N) {
+      const int64_t off = ((int64_t)kr * Hkv + hk) * D + part * 8;
+      kv4 = *reinterpret_cast<const u32x4*>(k + off);
+      vv4 = *reinterpret_cast<const u32x4*>(v + off);
     }
+    *reinterpret_cast<u32x4*>(smem + C::K_LDS + r * C::KSTR + part * 16) = kv4;
+    *reinterpret_cast<u32x4*>(smem + C::V_LDS + r * C::KSTR + part * 16) = vv4;
   }
+
   f32x16 dkt[D / 32], dvt[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dkt[db][i] = 0.0f; dvt[db][i] = 0.0f; }
 
-  u32x4 rq[C::RPT], rdo[C::RPT], rqt[C::TPT], rdot[C::TPT];
+  u32x4 rq[C::RPT], rdo[C::RPT];
   float a_lse = 0.0f, a_dl = 0.0f;
   int a_row = -1, a_ds = 0;
   auto gload = [&](int tq) {
@@ -155,13 +207,6 @@ __global__ void __launch_bounds__(NW * 64) dkdv_kernel(
         rdo[i] = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    const int64_t tb = ((int64_t)hk * ncb + tq) * (int64_t)(D * C::BQ);
-#pragma unroll
-    for (int i = 0; i < C::TPT; ++i) {
-      const int ch = tid + i * C::kThreads;
-      rqt[i] = *reinterpret_cast<const u32x4*>(qt + tb + ch * 8);
-      rdot[i] = *reinterpret_cast<const u32x4*>(dot + tb + ch * 8);
-    }
     if (tid < C::BQ) {
       const int64_t c = tc0 + tid;
       if (c < NG) {
@@ -179,25 +224,18 @@ __global__ void __launch_bounds__(NW * 64) dkdv_kernel(
       }
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int st) {
+    char* b = smem + st * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) {
       const int ch = tid + i * C::kThreads;
       const int r = ch / (D / 8), part = ch % (D / 8);
-      const int rp = (r & 32) | perm_row(r & 31);
-      *reinterpret_cast<u32x4*>(smem + C::Q_OFF + rp * C::RSTR + part * 16) = rq[i];
-      *reinterpret_cast<u32x4*>(smem + C::DO_OFF + rp * C::RSTR + part * 16) = rdo[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::TPT; ++i) {
-      const int ch = tid + i * C::kThreads;
-      const int d = ch / (C::BQ / 8), part = ch % (C::BQ / 8);
-      *reinterpret_cast<u32x4*>(smem + C::QT_OFF + d * C::TSTR + part * 16) = rqt[i];
-      *reinterpret_cast<u32x4*>(smem + C::DOT_OFF + d * C::TSTR + part * 16) = rdot[i];
+      *reinterpret_cast<u32x4*>(b + C::Q_OFF + lds_off<D>(tile_row(r), part)) = rq[i];
+      *reinterpret_cast<u32x4*>(b + C::DO_OFF + lds_off<D>(tile_row(r), part)) = rdo[i];
     }
     if (tid < C::BQ) {
-      float* af = reinterpret_cast<float*>(smem + C::AUX_OFF);
-      int* ai = reinterpret_cast<int*>(smem + C::AUX_OFF);
+      float* af = reinterpret_cast<float*>(b + C::AUX_OFF);
+      int* ai = reinterpret_cast<int*>(b + C::AUX_OFF);
       af[tid] = a_lse;
       af[C::BQ + tid] = a_dl;
       ai[2 * C::BQ + tid] = a_row;
@@ -205,90 +243,119 @@ __global__ void __launch_bounds__(NW * 64) dkdv_kernel(
     }
   };
 
-  gload(tq_lo);
-  lstore();
+  // Query tiles are visited from the document end downwards: the work-groups
+  // resident at the same time hold adjacent key blocks, so they all start at
+  // the same tile and stream the same Q / dO tiles through L2 in step.
+  gload(tq_hi);
+  lstore(0);
   __syncthreads();
-  const float* aux_lse = reinterpret_cast<const float*>(smem + C::AUX_OFF);
-  const float* aux_dl = aux_lse + C::BQ;
-  const int* aux_row = reinterpret_cast<const int*>(smem + C::AUX_OFF) + 2 * C::BQ;
-  const int* aux_ds = aux_row + C::BQ;
-  for (int tq = tq_lo; tq <= tq_hi; ++tq) {
-    if (tq < tq_hi) gload(tq + 1);
+  const char* kl = smem + C::K_LDS + (kbw * 32 + lc) * C::KSTR + g * 16;
+  const char* vl = smem + C::V_LDS + (kbw * 32 + lc) * C::KSTR + g * 16;
+  for (int tq = tq_hi; tq >= tq_lo; --tq) {
+    const int st = (tq_hi - tq) & 1;
+    if (tq > tq_lo) gload(tq - 1);
+    const char* b = smem + st * C::STAGE;
+    const float* aux_lse = reinterpret_cast<const float*>(b + C::AUX_OFF);
+    const float* aux_dl = aux_lse + C::BQ;
+    const int* aux_row = reinterpret_cast<const int*>(b + C::AUX_OFF) + 2 * C::BQ;
+    const int* aux_ds = aux_row + C::BQ;
     const int64_t tc0 = (int64_t)tq * C::BQ;
     const int first_row = (int)(tc0 >> lgG);
     const int last_row = (int)(min<int64_t>(NG - 1, tc0 + C::BQ - 1) >> lgG);
     const bool need_mask = first_row < kb_last || doc_start[last_row] > kb0 || tc0 + C::BQ > NG;
+
+    f32x16 s, dp;
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      f32x16 s, dp;
+    for (int i = 0; i < 16; ++i) { s[i] = 0.0f; dp[i] = 0.0f; }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { s[i] = 0.0f; dp[i] = 0.0f; }
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(b + C::Q_OFF + lds_off<D>(qh * 32 + lc, ks * 2 + g));
+      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(kl + ks * 32);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, s, 0, 0, 0);
+      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(b + C::DO_OFF + lds_off<D>(qh * 32 + lc, ks * 2 + g));
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vl + ks * 32);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, dp, 0, 0, 0);
+    }
+    // register i holds query column qh*32 + (i>>3)*16 + g*8 + (i&7) of the tile
+    f32x16 pr, dsr;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(smem + C::Q_OFF + (qh * 32 + lc) * C::RSTR + ks * 32 + g * 16);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s, 0, 0, 0);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(smem + C::DO_OFF + (qh * 32 + lc) * C::RSTR + ks * 32 + g * 16);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dp, 0, 0, 0);
-      }
-      // register i holds query column qh*32 + (i>>3)*16 + g*8 + (i&7) of the tile
-      f32x16 pr, dsr;
+    for (int half = 0; half < 2; ++half) {
+      const int cb = qh * 32 + half * 16 + g * 8;
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(aux_lse + cb);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(aux_lse + cb + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(aux_dl + cb);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(aux_dl + cb + 4);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int cb = qh * 32 + half * 16 + g * 8;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(aux_lse + cb);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(aux_lse + cb + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(aux_dl + cb);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(aux_dl + cb + 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = half * 8 + e;
-          const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float dv_ = e < 4 ? d0[e] : d1[e - 4];
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -lv));
-          if (need_mask) {
-            const int row = aux_row[cb + e];
-            if (!(key <= row && key >= aux_ds[cb + e])) p = 0.0f;
-          }
-          pr[i] = p;
-          dsr[i] = p * (dp[i] - dv_);
+      for (int e = 0; e < 8; ++e) {
+        const int i = half * 8 + e;
+        const float lv = e < 4 ? l0[e] : l1[e - 4];
+        const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -lv));
+        if (need_mask) {
+          const int row = aux_row[cb + e];
+          if (!(key <= row && key >= aux_ds[cb + e])) p = 0.0f;
         }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 bp = pack8(pr, kk * 8);
-        const bf16x8 bs = pack8(dsr, kk * 8);
-        const int qoff = (qh * 32 + kk * 16 + g * 8) * 2;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 adot = *reinterpret_cast<const bf16x8*>(smem + C::DOT_OFF + (db * 32 + lc) * C::TSTR + qoff);
-          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adot, bp, dvt[db], 0, 0, 0);
-          const bf16x8 aqt = *reinterpret_cast<const bf16x8*>(smem + C::QT_OFF + (db * 32 + lc) * C::TSTR + qoff);
-          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, bs, dkt[db], 0, 0, 0);
-        }
+        pr[i] = p;
+        dsr[i] = p * (dp[i] - dv_);
       }
     }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 bp = pack8(pr, kk * 8);
+      const bf16x8 bs = pack8(dsr, kk * 8);
+      const int k0 = qh * 32 + kk * 16;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 adot = lds_tr_a<D>(b + C::DO_OFF, db * 32, k0, l);
+        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adot, bp, dvt[db], 0, 0, 0);
+        const bf16x8 aqt = lds_tr_a<D>(b + C::Q_OFF, db * 32, k0, l);
+        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, bs, dkt[db], 0, 0, 0);
+      }
+    }
+    if (tq > tq_lo) lstore(st ^ 1);
     __syncthreads();
-    if (tq < tq_hi) {
-      lstore();
+  }
+
+  // sum the two halves: the upper waves hand their partial sums to the lower
+  // ones through LDS (dK^T first, then dV^T)
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          red[((kbw * (D / 32) + db) * 16 + i) * 64 + l] = which == 0 ? dkt[db][i] : dvt[db][i];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = red[((kbw * (D / 32) + db) * 16 + i) * 64 + l];
+          if (which == 0) dkt[db][i] += x; else dvt[db][i] += x;
+        }
     }
     __syncthreads();
   }
 
-  if (kvalid) {
+  if (qh == 0 && kvalid) {
     const int64_t base = ((int64_t)key * Hkv + hk) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = db * 32 + j * 8 + g * 4;
-        f32x4 a, b;
+        f32x4 a, bb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           a[e] = dkt[db][j * 4 + e] * scale;
-          b[e] = dvt[db][j * 4 + e];
+          bb[e] = dvt[db][j * 4 + e];
         }
         *reinterpret_cast<f32x4*>(dk + base + d) = a;
-        *reinterpret_cast<f32x4*>(dv + base + d) = b;
+        *reinterpret_cast<f32x4*>(dv + base + d) = bb;
       }
   }
 }
@@ -299,25 +366,21 @@ struct DqCfg {
   static constexpr int kThreads = NW * 64;
   static constexpr int BN = 64;            // keys per tile
   static constexpr int BMC = NW * 32;      // query columns per work-group
-  static constexpr int RSTR = D * 2 + 16;  // LDS bytes per K / V row
-  static constexpr int TSTR = BN * 2 + 16; // LDS bytes per K^T row
+  static constexpr int RSTR = D * 2;       // LDS bytes per K / V row (swizzled, unpadded)
   static constexpr int RBYTES = BN * RSTR;
-  static constexpr int TBYTES = D * TSTR;
-  static constexpr int K_OFF = 0, V_OFF = RBYTES, KT_OFF = 2 * RBYTES;
-  static constexpr int STAGE = 2 * RBYTES + TBYTES;
+  static constexpr int K_OFF = 0, V_OFF = RBYTES;
+  static constexpr int STAGE = 2 * RBYTES;
   static constexpr int RCH = BN * D / 8;
-  static constexpr int TCH = D * BN / 8;
   static constexpr int RPT = RCH / kThreads;
-  static constexpr int TPT = TCH / kThreads;
-  static_assert(RCH % kThreads == 0 && TCH % kThreads == 0, "tile chunks must split evenly");
+  static_assert(RCH % kThreads == 0, "tile chunks must split evenly");
 };
 
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64) dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    const bf16* __restrict__ kt, const int32_t* __restrict__ doc_start, float* __restrict__ dq, int N, int Hkv,
-    int lgG, float sl2, float scale, int ncb, int nb) {
+    const int32_t* __restrict__ doc_start, float* __restrict__ dq, int N, int Hkv, int lgG, float sl2,
+    float scale, int ncb) {
   using C = DqCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
@@ -360,7 +423,7 @@ __global__ void __launch_bounds__(NW * 64) dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
 
-  u32x4 rk[C::RPT], rv[C::RPT], rkt[C::TPT];
+  u32x4 rk[C::RPT], rv[C::RPT];
   auto gload = [&](int t) {
     const int t0 = t * C::BN;
 #pragma unroll
@@ -377,12 +440,6 @@ __global__ void __launch_bounds__(NW * 64) dq_kernel(
         rv[i] = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    const bf16* src = kt + ((int64_t)hk * nb + t) * (int64_t)(D * C::BN);
-#pragma unroll
-    for (int i = 0; i < C::TPT; ++i) {
-      const int ch = tid + i * C::kThreads;
-      rkt[i] = *reinterpret_cast<const u32x4*>(src + ch * 8);
-    }
   };
   auto lstore = [&](int st) {
     char* b = smem + st * C::STAGE;
@@ -390,15 +447,8 @@ __global__ void __launch_bounds__(NW * 64) dq_kernel(
     for (int i = 0; i < C::RPT; ++i) {
       const int ch = tid + i * C::kThreads;
       const int r = ch / (D / 8), part = ch % (D / 8);
-      const int rp = (r & 32) | perm_row(r & 31);
-      *reinterpret_cast<u32x4*>(b + C::K_OFF + rp * C::RSTR + part * 16) = rk[i];
-      *reinterpret_cast<u32x4*>(b + C::V_OFF + rp * C::RSTR + part * 16) = rv[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::TPT; ++i) {
-      const int ch = tid + i * C::kThreads;
-      const int d = ch / (C::BN / 8), part = ch % (C::BN / 8);
-      *reinterpret_cast<u32x4*>(b + C::KT_OFF + d * C::TSTR + part * 16) = rkt[i];
+      *reinterpret_cast<u32x4*>(b + C::K_OFF + lds_off<D>(tile_row(r), part)) = rk[i];
+      *reinterpret_cast<u32x4*>(b + C::V_OFF + lds_off<D>(tile_row(r), part)) = rv[i];
     }
   };
 
@@ -416,9 +466,9 @@ __global__ void __launch_bounds__(NW * 64) dq_kernel(
       for (int i = 0; i < 16; ++i) { s[kb][i] = 0.0f; dp[kb][i] = 0.0f; }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(b + C::K_OFF + (kb * 32 + lc) * C::RSTR + ks * 32 + g * 16);
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(b + C::K_OFF + lds_off<D>(kb * 32 + lc, ks * 2 + g));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], s[kb], 0, 0, 0);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(b + C::V_OFF + (kb * 32 + lc) * C::RSTR + ks * 32 + g * 16);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(b + C::V_OFF + lds_off<D>(kb * 32 + lc, ks * 2 + g));
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[ks], dp[kb], 0, 0, 0);
       }
     }
@@ -440,7 +490,7 @@ __global__ void __launch_bounds__(NW * 64) dq_kernel(
       const bf16x8 bs = pack8(s[tt >> 1], (tt & 1) * 8);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(b + C::KT_OFF + (db * 32 + lc) * C::TSTR + tt * 32 + g * 16);
+        const bf16x8 a = lds_tr_a<D>(b + C::K_OFF, db * 32, tt * 16, l);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, acc[db], 0, 0, 0);
       }
     }
@@ -471,13 +521,12 @@ int ilog2_pow2(int x) {
 
 hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o, const bf16* dout,
                                 const float* lse, const int32_t* doc_start, const int32_t* doc_end, float* dq,
-                                float* dk, float* dv, float* delta, bf16* qt, bf16* dot, bf16* kt, int N, int Hq,
-                                int Hkv, int D, float scale, hipStream_t s) {
+                                float* dk, float* dv, float* delta, int N, int Hq, int Hkv, int D, float scale,
+                                hipStream_t s) {
   const int G = Hq / Hkv;
   const int lgG = ilog2_pow2(G);
   const int64_t NG = (int64_t)N * G;
   const float sl2 = scale * kLog2e;
-  // pre-passes: delta, blocked transposes of Q, dO (query columns) and K (keys)
   {
     const int cpb = 256 / (D / 8);
     const dim3 grid((unsigned)((NG + cpb - 1) / cpb), Hkv);
@@ -489,26 +538,17 @@ hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_transpose_blocked(q, qt, NG, Hq, Hkv, lgG, D, s);
-  if (e != hipSuccess) return e;
-  e = launch_transpose_blocked(dout, dot, NG, Hq, Hkv, lgG, D, s);
-  if (e != hipSuccess) return e;
-  e = launch_transpose_blocked(k, kt, N, Hkv, Hkv, 0, D, s);
-  if (e != hipSuccess) return e;
-  const int ncb_t = (int)((NG + kTB - 1) / kTB);  // blocked column tiles of the transposed copies
-  const int nb = (N + kTB - 1) / kTB;
   {
-    constexpr int NW = 4;
-    const int nkb = (N + NW * 32 - 1) / (NW * 32);
-    const dim3 grid((unsigned)((int64_t)nkb * Hkv)), block(NW * 64);
+    const int nkb = (N + DkvCfg<128>::BNK - 1) / DkvCfg<128>::BNK;
+    const dim3 grid((unsigned)((int64_t)nkb * Hkv));
     TimedLaunch timer("attn_bwd_dkdv", s);
     if (D == 128)
-      hipLaunchKernelGGL((dkdv_kernel<128, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, qt, dot, doc_start,
-                         doc_end, dk, dv, N, Hkv, lgG, sl2, scale, nkb, ncb_t);
+      hipLaunchKernelGGL(dkdv_kernel<128>, grid, dim3(DkvCfg<128>::kThreads), 0, s, q, k, v, dout, lse, delta,
+                         doc_start, doc_end, dk, dv, N, Hkv, lgG, sl2, scale);
     else
-      hipLaunchKernelGGL((dkdv_kernel<64, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, qt, dot, doc_start,
-                         doc_end, dk, dv, N, Hkv, lgG, sl2, scale, nkb, ncb_t);
-    e = hipGetLastError();
+      hipLaunchKernelGGL(dkdv_kernel<64>, grid, dim3(DkvCfg<64>::kThreads), 0, s, q, k, v, dout, lse, delta,
+                         doc_start, doc_end, dk, dv, N, Hkv, lgG, sl2, scale);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
@@ -517,11 +557,11 @@ hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, con
     const dim3 grid((unsigned)((int64_t)ncb * Hkv)), block(NW * 64);
     TimedLaunch timer("attn_bwd_dq", s);
     if (D == 128)
-      hipLaunchKernelGGL((dq_kernel<128, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, kt, doc_start, dq, N,
-                         Hkv, lgG, sl2, scale, ncb, nb);
+      hipLaunchKernelGGL((dq_kernel<128, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, doc_start, dq, N, Hkv,
+                         lgG, sl2, scale, ncb);
     else
-      hipLaunchKernelGGL((dq_kernel<64, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, kt, doc_start, dq, N,
-                         Hkv, lgG, sl2, scale, ncb, nb);
+      hipLaunchKernelGGL((dq_kernel<64, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, doc_start, dq, N, Hkv,
+                         lgG, sl2, scale, ncb);
   }
   return hipGetLastError();
 }

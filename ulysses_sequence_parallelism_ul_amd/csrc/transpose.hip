@@ -1,8 +1,7 @@
 // Blocked transposed copies of attention operands, kept in the workspace.
 //
-// The MFMA contractions of attention over the token axis (P.V in the forward;
-// dO^T.P, Q^T.dS and K^T.dS in the backward) need their token-major operand
-// with tokens as the fast axis.  One pass per call rewrites a [cols][D] bf16
+// The forward's P.V contraction runs over the token axis and needs V with
+// tokens as the fast axis.  One pass per call rewrites a [cols][D] bf16
 // matrix view into tiles [cols / kTB][D][kTB] (zero-padded past the last
 // column), so a kTB x D tile is one contiguous 16 KiB block that the
 // attention kernels stream into LDS with plain 16-byte loads.  This is

@@ -32,9 +32,6 @@ struct WsLayout {
   size_t doc_start = 0, doc_end = 0, scan = 0;  // int32 [N], int32 [N], int32 [2 * nblk]
   size_t vt = 0;     // bf16 fwd: V^T blocked [Hkv][NB][D][kTB]
   size_t delta = 0;  // bwd: float [Hkv][N*G] (query-column order)
-  size_t qt = 0;     // bf16 bwd: Q^T blocked  [Hkv][CB][D][kTB]
-  size_t dot = 0;    // bf16 bwd: dO^T blocked [Hkv][CB][D][kTB]
-  size_t kt = 0;     // bf16 bwd: K^T blocked  [Hkv][NB][D][kTB]
   size_t total = 0;
 };
 
@@ -74,8 +71,7 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, c
 hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
                                 const bf16* dout, const float* lse, const int32_t* doc_start,
                                 const int32_t* doc_end, float* dq, float* dk, float* dv, float* delta,
-                                bf16* qt, bf16* dot, bf16* kt, int N, int Hq, int Hkv, int D,
-                                float scale, hipStream_t s);
+                                int N, int Hq, int Hkv, int D, float scale, hipStream_t s);
 hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                                const float* dout, const float* lse, const int32_t* doc_start,
                                const int32_t* doc_end, float* dq, float* dk, float* dv, float* delta,
