@@ -197,31 +197,21 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     for (int i = 0; i < C::RPT; ++i) {
       const int ch = tid + i * C::kThreads;
       const int r = ch / (D / 8), part = ch % (D / 8);
-      const int64_t c = tc0 + r;
-      if (c < NG) {
-        const int64_t off = col_offset(c, lgG, Hkv, hk, D) + part * 8;
-        rq[i] = *reinterpret_cast<const u32x4*>(q + off);
-        rdo[i] = *reinterpret_cast<const u32x4*>(dout + off);
-      } else {
-        rq[i] = u32x4{0u, 0u, 0u, 0u};
-        rdo[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      // columns past the end read the last column instead (their P and dS are
+      // masked to zero), so the loads carry no branch
+      const int64_t c = min<int64_t>(tc0 + r, NG - 1);
+      const int64_t off = col_offset(c, lgG, Hkv, hk, D) + part * 8;
+      rq[i] = *reinterpret_cast<const u32x4*>(q + off);
+      rdo[i] = *reinterpret_cast<const u32x4*>(dout + off);
     }
     if (tid < C::BQ) {
-      const int64_t c = tc0 + tid;
-      if (c < NG) {
-        const int row = (int)(c >> lgG);
-        const int h = (hk << lgG) + (int)(c & (G - 1));
-        a_lse = lse[(int64_t)h * N + row] * kLog2e;
-        a_dl = delta[(int64_t)hk * NG + c];
-        a_row = row;
-        a_ds = doc_start[row];
-      } else {
-        a_lse = 0.0f;
-        a_dl = 0.0f;
-        a_row = -1;
-        a_ds = 0;
-      }
+      const int64_t c = min<int64_t>(tc0 + tid, NG - 1);
+      const int row = (int)(c >> lgG);
+      const int h = (hk << lgG) + (int)(c & (G - 1));
+      a_lse = lse[(int64_t)h * N + row];  // scaled by log2(e) when stored, after the load has landed
+      a_dl = delta[(int64_t)hk * NG + c];
+      a_row = tc0 + tid < NG ? row : -1;  // -1 masks the column out
+      a_ds = doc_start[row];
     }
   };
   auto lstore = [&](int st) {
@@ -236,7 +226,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     if (tid < C::BQ) {
       float* af = reinterpret_cast<float*>(b + C::AUX_OFF);
       int* ai = reinterpret_cast<int*>(b + C::AUX_OFF);
-      af[tid] = a_lse;
+      af[tid] = a_lse * kLog2e;
       af[C::BQ + tid] = a_dl;
       ai[2 * C::BQ + tid] = a_row;
       ai[3 * C::BQ + tid] = a_ds;
@@ -290,15 +280,24 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
         const int i = half * 8 + e;
         const float lv = e < 4 ? l0[e] : l1[e - 4];
         const float dv_ = e < 4 ? d0[e] : d1[e - 4];
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -lv));
-        if (need_mask) {
-          const int row = aux_row[cb + e];
-          if (!(key <= row && key >= aux_ds[cb + e])) p = 0.0f;
-        }
-        pr[i] = p;
-        dsr[i] = p * (dp[i] - dv_);
+        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -lv));
+        dsr[i] = dp[i] - dv_;
       }
     }
+    // one uniform branch around the masking of the whole tile (branch-free inside)
+    if (need_mask) {
+      typedef int i32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int cb = qh * 32 + (q4 >> 1) * 16 + g * 8 + (q4 & 1) * 4;
+        const i32x4 rr = *reinterpret_cast<const i32x4*>(aux_row + cb);
+        const i32x4 dd = *reinterpret_cast<const i32x4*>(aux_ds + cb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[q4 * 4 + e] = (key <= rr[e] && key >= dd[e]) ? pr[q4 * 4 + e] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dsr[i] *= pr[i];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const bf16x8 bp = pack8(pr, kk * 8);
@@ -430,15 +429,11 @@ __global__ void __launch_bounds__(NW * 64) dq_kernel(
     for (int i = 0; i < C::RPT; ++i) {
       const int ch = tid + i * C::kThreads;
       const int r = ch / (D / 8), part = ch % (D / 8);
-      const int kv = t0 + r;
-      if (kv < N) {
-        const int64_t off = ((int64_t)kv * Hkv + hk) * D + part * 8;
-        rk[i] = *reinterpret_cast<const u32x4*>(k + off);
-        rv[i] = *reinterpret_cast<const u32x4*>(v + off);
-      } else {
-        rk[i] = u32x4{0u, 0u, 0u, 0u};
-        rv[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      // keys past the end read the last key instead (their P is masked to zero)
+      const int kv = min(t0 + r, N - 1);
+      const int64_t off = ((int64_t)kv * Hkv + hk) * D + part * 8;
+      rk[i] = *reinterpret_cast<const u32x4*>(k + off);
+      rv[i] = *reinterpret_cast<const u32x4*>(v + off);
     }
   };
   auto lstore = [&](int st) {
@@ -459,39 +454,41 @@ __global__ void __launch_bounds__(NW * 64) dq_kernel(
     const int st = (t - t_lo) & 1;
     if (t < t_hi) gload(t + 1);
     const char* b = smem + st * C::STAGE;
-    f32x16 s[2], dp[2];
+    const int t0 = t * C::BN;
+    const bool need_mask = t0 + C::BN - 1 > r_first || t0 < ds_last;
+    // the two 32-key halves one after the other: S^T, dP^T, dS^T, then dQ^T += K^T dS^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { s[kb][i] = 0.0f; dp[kb][i] = 0.0f; }
+      for (int i = 0; i < 16; ++i) { s[i] = 0.0f; dp[i] = 0.0f; }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 ak = *reinterpret_cast<const bf16x8*>(b + C::K_OFF + lds_off<D>(kb * 32 + lc, ks * 2 + g));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], s[kb], 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], s, 0, 0, 0);
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(b + C::V_OFF + lds_off<D>(kb * 32 + lc, ks * 2 + g));
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[ks], dp[kb], 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[ks], dp, 0, 0, 0);
       }
-    }
-    const int t0 = t * C::BN;
-    const bool need_mask = t0 + C::BN - 1 > r_first || t0 < ds_last;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -lse2));
+      // one uniform branch around the masking (branch-free inside)
+      if (need_mask) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], sl2, -lse2));
-        if (need_mask) {
+        for (int i = 0; i < 16; ++i) {
           const int kv = t0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-          if (!(kv <= row && kv >= ds_c)) p = 0.0f;
+          s[i] = (kv <= row && kv >= ds_c) ? s[i] : 0.0f;
         }
-        s[kb][i] = p * (dp[kb][i] - dl);  // dS^T
       }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const bf16x8 bs = pack8(s[tt >> 1], (tt & 1) * 8);
+      for (int i = 0; i < 16; ++i) s[i] *= dp[i] - dl;  // dS^T
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = lds_tr_a<D>(b + C::K_OFF, db * 32, tt * 16, l);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, acc[db], 0, 0, 0);
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 bs = pack8(s, half * 8);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 a = lds_tr_a<D>(b + C::K_OFF, db * 32, kb * 32 + half * 16, l);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, acc[db], 0, 0, 0);
+        }
       }
     }
     if (t < t_hi) lstore(st ^ 1);

@@ -70,6 +70,19 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   return r;
 }
 
+// Combine a value across the lane pair (l, l ^ 32) with v_permlane32_swap
+// (no LDS round trip): after the swap one result holds lane (l & 31)'s value
+// and the other lane (l | 32)'s, so the symmetric combination is the same on
+// both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ vt,
@@ -122,11 +135,10 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_bf16_kernel(
     for (int i = 0; i < C::KPT; ++i) {
       const int ch = tid + i * C::kThreads;
       const int r = ch / (D / 8), part = ch % (D / 8);
-      const int kv = t0 + r;
-      if (kv < N)
-        kpre[i] = *reinterpret_cast<const u32x4*>(k + ((int64_t)kv * Hkv + hk) * D + part * 8);
-      else
-        kpre[i] = u32x4{0u, 0u, 0u, 0u};
+      // keys past the end read the last key instead (masked out below), so the
+      // loads carry no branch
+      const int kv = min(t0 + r, N - 1);
+      kpre[i] = *reinterpret_cast<const u32x4*>(k + ((int64_t)kv * Hkv + hk) * D + part * 8);
     }
     const bf16* vsrc = vt + ((int64_t)hk * nb + t) * (int64_t)(D * C::BN);
 #pragma unroll
@@ -190,7 +202,7 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = pair_max(mx);
     const float mnew = mx * sl2;
     const bool up = mnew > m_run + kRescaleSlack;
     if (__any(up)) {
@@ -230,7 +242,7 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_bf16_kernel(
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   if (cvalid) {
     const float inv = 1.0f / l_tot;
 #pragma unroll
