@@ -311,6 +311,14 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
         dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, bs, dkt[db], 0, 0, 0);
       }
     }
+    // schedule: 4 transpose reads in flight ahead of the dV/dK MFMAs (two per MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int j = 0; j < D / 8 - 2; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     if (tq > tq_lo) lstore(st ^ 1);
     __syncthreads();
   }

@@ -185,6 +185,22 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_bf16_kernel(
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
       }
     }
+    // schedule: 8 K reads in flight ahead of the 16 MFMAs (the compiler's own
+    // order waits on each read right before its MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 LDS reads
+#pragma unroll
+    for (int j = 0; j < 2 * (D / 16) - 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    // the first two 16-key steps of V^T travel during the softmax
+    bf16x8 va[2][D / 32];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        va[tt][db] = *reinterpret_cast<const bf16x8*>(vb_l + (db * 32 + lc) * C::VSTR + tt * 32 + g * 16);
 
     const int t0 = t * C::BN;
     if (t0 + C::BN - 1 > r_first || t0 < ds_last) {
@@ -233,7 +249,8 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_bf16_kernel(
       const bf16x8 pb = pack8(s[tt >> 1], (tt & 1) * 8);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb_l + (db * 32 + lc) * C::VSTR + tt * 32 + g * 16);
+        const bf16x8 a =
+            tt < 2 ? va[tt][db] : *reinterpret_cast<const bf16x8*>(vb_l + (db * 32 + lc) * C::VSTR + tt * 32 + g * 16);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
       }
     }
