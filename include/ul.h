@@ -152,6 +152,51 @@ ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o
                       float scale, ul_dtype dt, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The whole per-rank path in one call each way, optionally in head chunks.
+ * Head chunking (the "UPipe" row of the comparison table on page
+ * "Ulysses 序列並行：百萬 Token 上下文訓練", setupai.cc, section "競品分析":
+ * attention split by heads to cut activation memory) runs the rank's Hq/P
+ * query heads as `chunks` chunks of consecutive heads, so only one chunk's
+ * head-layout buffers are live at a time.  Each chunk is the same three steps
+ * as the separate calls above: seq->head of its Q (and K/V) columns,
+ * attention, head->seq of its outputs.
+ *   q_seq [N][Hq][D], k_seq / v_seq [N][Hkv][D] of type dt: the P sequence
+ *     shards stacked (as ul_seq_to_head's x_seq), read only.
+ *   position_ids [N] int32 or NULL, scale: as ul_attn_fwd.
+ *   P, rank: the emulated rank count and this rank; Hq, Hkv and N must be
+ *     multiples of P (no KV-head replication).
+ *   chunks: divides Hq/P; a chunk's q heads either cover whole groups of
+ *     G = Hq/Hkv heads (then its KV heads are chunked too) or divide one group
+ *     (then consecutive chunks share their KV head and its dK / dV partials are
+ *     summed in chunk order).  chunks = 1 is the unchunked path.
+ *   ws / ws_bytes: at least ul_rank_workspace_bytes(...) bytes, caller-owned;
+ *     it holds one chunk's head-layout buffers and the attention workspace.
+ * ul_rank_attn_fwd writes rank `rank`'s columns of o_seq [N][Hq][D] (type dt;
+ * other columns untouched) and lse [Hq/P][N] float (natural log, the rank's
+ * heads in order).  ul_rank_attn_bwd takes o_seq and lse from it and
+ * do_seq [N][Hq][D] (type dt), and writes the rank's columns of the float
+ * gradients dq_seq [N][Hq][D], dk_seq and dv_seq [N][Hkv][D].  For one chunk
+ * the results are bit-identical to ul_seq_to_head + ul_attn_fwd/bwd +
+ * ul_head_to_seq; with chunks sharing a KV head, dK and dV differ by the
+ * summation order only.
+ * Errors: UL_ERR_ARG for the shape rules above, a chunking that fits neither
+ * case, null, misaligned or overlapping outputs, a workspace too small;
+ * UL_ERR_UNSUPPORTED as ul_attn_fwd (applied to one chunk's shapes).  All
+ * checks run before anything is enqueued.
+ */
+size_t ul_rank_workspace_bytes(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t chunks,
+                               ul_dtype dt, int32_t for_bwd);
+ul_status ul_rank_attn_fwd(const void *q_seq, const void *k_seq, const void *v_seq,
+                           const int32_t *position_ids, void *o_seq, float *lse, int64_t N, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t P, int32_t rank, int32_t chunks, float scale,
+                           ul_dtype dt, void *ws, size_t ws_bytes, void *stream);
+ul_status ul_rank_attn_bwd(const void *q_seq, const void *k_seq, const void *v_seq, const void *o_seq,
+                           const void *do_seq, const float *lse, const int32_t *position_ids,
+                           float *dq_seq, float *dk_seq, float *dv_seq, int64_t N, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t P, int32_t rank, int32_t chunks, float scale,
+                           ul_dtype dt, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Optional per-kernel timing for benchmarks.  While enabled, every kernel the
  * library launches is bracketed by two hipEvents recorded on the kernel's own
  * stream; elapsed times are summed per kernel name.  Off by default.

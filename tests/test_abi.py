@@ -123,3 +123,47 @@ def test_attn_bwd_rejections():
     assert bwd(wsb=16) == ul.UL_ERR_ARG
     assert bwd(dq=None) == ul.UL_ERR_ARG
     assert bwd(dk=G_) == ul.UL_ERR_ARG  # dk overlaps dq
+
+
+def test_rank_workspace_and_rejections():
+    lib = ul.load()
+    # valid: the million-token training share at 1, 2 and 4 head chunks; linear in N
+    for chunks in (1, 2, 4):
+        for bwd in (0, 1):
+            w1 = lib.ul_rank_workspace_bytes(1 << 16, 32, 8, 128, 8, chunks, ul.UL_BF16, bwd)
+            w2 = lib.ul_rank_workspace_bytes(1 << 17, 32, 8, 128, 8, chunks, ul.UL_BF16, bwd)
+            assert w1 > 0 and abs(w2 - 2 * w1) <= 8192
+    # fewer heads per chunk, smaller workspace
+    assert (lib.ul_rank_workspace_bytes(1 << 16, 32, 8, 128, 8, 4, ul.UL_BF16, 0)
+            < lib.ul_rank_workspace_bytes(1 << 16, 32, 8, 128, 8, 1, ul.UL_BF16, 0))
+    bad = [
+        (1024, 32, 8, 128, 8, 3),    # 3 chunks do not divide 4 query heads
+        (1024, 24, 6, 128, 2, 2),    # 6 query heads per chunk vs groups of 4: neither divides
+        (1024, 32, 4, 128, 8, 1),    # 4 KV heads over 8 ranks (replication)
+        (1020, 32, 8, 128, 8, 1),    # N not a multiple of P
+        (1024, 32, 8, 96, 8, 1),     # head dim
+        (1024, 32, 8, 128, 0, 1),    # P
+        (1024, 32, 8, 128, 8, 0),    # chunks
+    ]
+    for N, Hq, Hkv, D, P, chunks in bad:
+        assert lib.ul_rank_workspace_bytes(N, Hq, Hkv, D, P, chunks, ul.UL_F32, 0) == 0, (Hq, Hkv, P, chunks)
+
+    def fwd(N=64, Hq=32, Hkv=8, P=8, rank=0, chunks=1, wsb=1 << 30, q=A, o=D_, lse=E):
+        return lib.ul_rank_attn_fwd(q, B, C, None, o, lse, N, Hq, Hkv, 128, P, rank, chunks, 0.1, ul.UL_BF16, F, wsb,
+                                    None)
+
+    assert fwd(chunks=3) == ul.UL_ERR_ARG and "chunks" in _err()
+    assert fwd(rank=8) == ul.UL_ERR_ARG and "rank" in _err()
+    assert fwd(N=60) == ul.UL_ERR_ARG
+    assert fwd(wsb=1024) == ul.UL_ERR_ARG and "workspace" in _err()
+    assert fwd(q=None) == ul.UL_ERR_ARG
+    assert fwd(o=A) == ul.UL_ERR_ARG  # output overlaps q_seq
+    assert fwd(lse=A + 8) == ul.UL_ERR_ARG
+
+    def bwd(chunks=1, dq=G_, dk=H_, wsb=1 << 30):
+        return lib.ul_rank_attn_bwd(A, B, C, D_, E, F, None, dq, dk, I_, 64, 32, 8, 128, 8, 0, chunks, 0.1,
+                                    ul.UL_BF16, J, wsb, None)
+
+    assert bwd(chunks=8) == ul.UL_ERR_ARG
+    assert bwd(dk=G_) == ul.UL_ERR_ARG  # dk overlaps dq
+    assert bwd(wsb=64) == ul.UL_ERR_ARG

@@ -1,0 +1,127 @@
+"""GPU tests of the rank-level entry points (the whole per-rank path in one
+call each way, optionally in query-head chunks).
+
+The separate calls (seq->head, attention, head->seq) are parity-tested against
+the oracle elsewhere; here the rank path must reproduce them bit for bit
+wherever the arithmetic is the same (one chunk; chunks that own their KV
+heads; O, LSE and dQ always), and dK / dV of chunks that share a KV head (a
+different summation order) must match the fp64 oracle to the gradient bar.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ulysses_sequence_parallelism_ul_amd as ul
+from gpu_helpers import TOL_LSE, TOL_OUT, grad_bar, log, max_abs, np64, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(N, Hq, Hkv, D, seed, dtype):
+    host = synth.host_qkv(N, Hq, Hkv, D, seed, "bf16" if dtype == torch.bfloat16 else "f32", with_do=True)
+    return {k: v.to("cuda:0") for k, v in host.items()}, host
+
+
+def _separate(d, pos, P, rank):
+    """seq->head, attention, head->seq with the separate calls."""
+    qh, kh, vh, doh = (ul.seq_to_head(d[x], P, rank) for x in ("q", "k", "v", "do"))
+    oh, lse = ul.attn_fwd(qh, kh, vh, pos)
+    dqh, dkh, dvh = ul.attn_bwd(qh, kh, vh, oh, doh, lse, pos)
+    N, Hq, D = d["q"].shape
+    Hkv = d["k"].shape[1]
+    o = torch.zeros_like(d["q"])
+    dq = torch.zeros((N, Hq, D), dtype=torch.float32, device="cuda:0")
+    dk = torch.zeros((N, Hkv, D), dtype=torch.float32, device="cuda:0")
+    dv = torch.zeros_like(dk)
+    ul.head_to_seq(oh, o, P, rank)
+    ul.head_to_seq(dqh, dq, P, rank)
+    ul.head_to_seq(dkh, dk, P, rank)
+    ul.head_to_seq(dvh, dv, P, rank)
+    return o, lse, dq, dk, dv
+
+
+def _rank(d, pos, P, rank, chunks):
+    o, lse = ul.rank_attn_fwd(d["q"], d["k"], d["v"], P, rank, pos, chunks=chunks)
+    dq, dk, dv = ul.rank_attn_bwd(d["q"], d["k"], d["v"], o, d["do"], lse, P, rank, pos, chunks=chunks)
+    return o, lse, dq, dk, dv
+
+
+def _same(a, b):
+    return torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+# (N, Hq, Hkv, D, P, rank); the rank's share has hq = Hq/P q heads and hkv = Hkv/P KV heads
+SHAPES = [
+    (384, 8, 4, 128, 2, 1),     # hq 4, hkv 2, groups of 2: chunks 1, 2 (own KV), 4 (shared KV)
+    (320, 16, 2, 64, 2, 0),     # hq 8, hkv 1, a group of 8: chunks 1, 2, 4, 8 (shared KV)
+    (200, 4, 4, 128, 2, 1),     # hq 2, hkv 2, groups of 1: chunks 1, 2 (own KV)
+]
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,D,P,rank", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rank_path_against_separate_calls_and_oracle(N, Hq, Hkv, D, P, rank, dtype):
+    require_gpu()
+    hq, hkv = Hq // P, Hkv // P
+    G = hq // hkv
+    seed = 11 * N + Hq
+    d, host = _inputs(N, Hq, Hkv, D, seed, dtype)
+    pos_np = synth.random_positions(N, seed, max_docs=5)
+    pos = torch.from_numpy(pos_np).to("cuda:0")
+    ref_sep = _separate(d, pos, P, rank)
+    q64, k64, v64, do64 = (host[x].double().numpy() for x in ("q", "k", "v", "do"))
+    heads = slice(rank * hq, (rank + 1) * hq)
+    kvheads = slice(rank * hkv, (rank + 1) * hkv)
+    orc = oracle.attn_bwd(q64[:, heads], k64[:, kvheads], v64[:, kvheads], do64[:, heads], pos_np)
+    for chunks in [c for c in (1, 2, 4, 8) if hq % c == 0]:
+        log(f"rank path N={N} Hq={Hq} Hkv={Hkv} D={D} P={P} rank={rank} chunks={chunks} {dtype}")
+        got = _rank(d, pos, P, rank, chunks)
+        torch.cuda.synchronize()
+        shared = (hq // chunks) < G
+        for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, ref_sep):
+            if shared and name in ("dk", "dv"):
+                continue
+            assert _same(a, b), f"{name} differs from the separate calls at chunks={chunks}"
+        # other ranks' columns stay untouched (zero-filled by the binding)
+        for t in (got[0], got[2]):
+            mask = torch.ones(t.shape[1], dtype=torch.bool)
+            mask[heads] = False
+            assert not t[:, mask].any()
+        for name, gi, key in (("dk", 3, "dk"), ("dv", 4, "dv")):
+            g = np64(got[gi][:, kvheads])
+            tol = grad_bar(orc[key]) if dtype == torch.bfloat16 else 1e-4
+            assert max_abs(g, orc[key]) <= tol, (name, chunks)
+        assert max_abs(np64(got[1]), orc["lse"]) <= (TOL_LSE if dtype == torch.bfloat16 else 1e-4)
+        assert max_abs(np64(got[0][:, heads]), orc["o"]) <= (TOL_OUT if dtype == torch.bfloat16 else 1e-4)
+
+
+def test_rank_path_training_share_chunkings():
+    """The packed 256K-token training share (32 q / 8 KV heads over 8 ranks, rank 3): one, two and
+    four head chunks give bit-identical O, LSE and dQ; dK / dV (one KV head shared by the chunks)
+    agree to fp32 summation-order level."""
+    require_gpu()
+    w = synth.WORKLOADS["train_packed"]
+    N, Hq, Hkv, D, P, rank = w["N"], w["Hq"], w["Hkv"], w["D"], w["P"], 3
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(5)
+    d = {x: torch.randn((N, Hq if x in ("q", "do") else Hkv, D), device="cuda:0", generator=g).to(torch.bfloat16)
+         for x in ("q", "k", "v", "do")}
+    pos = torch.from_numpy(synth.workload_positions("train_packed")).to("cuda:0")
+    base = None
+    for chunks in (1, 2, 4):
+        log(f"training share rank path chunks={chunks}")
+        got = _rank(d, pos, P, rank, chunks)
+        torch.cuda.synchronize()
+        if base is None:
+            base = got
+            continue
+        for name, a, b in zip(("o", "lse", "dq"), got[:3], base[:3]):
+            assert _same(a, b), f"{name} differs between 1 and {chunks} chunks"
+        for name, a, b in zip(("dk", "dv"), got[3:], base[3:]):
+            diff = (a - b).abs().max().item()
+            scale = b.abs().max().item()
+            assert diff <= 1e-5 * max(1.0, scale), (name, chunks, diff, scale)

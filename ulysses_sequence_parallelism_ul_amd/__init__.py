@@ -26,6 +26,9 @@ __all__ = [
     "attn_workspace_bytes",
     "attn_fwd",
     "attn_bwd",
+    "rank_workspace_bytes",
+    "rank_attn_fwd",
+    "rank_attn_bwd",
     "timing_enable",
     "timing_reset",
     "timing_read",
@@ -59,6 +62,11 @@ SIGNATURES = {
     "ul_attn_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32]),
     "ul_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
     "ul_attn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
+    "ul_rank_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "ul_rank_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _SZ,
+                                _P]),
+    "ul_rank_attn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F,
+                                _I32, _P, _SZ, _P]),
     "ul_timing_enable": (_I32, [_I32]),
     "ul_timing_reset": (None, []),
     "ul_timing_read": (_I32, [_I32, ctypes.c_char_p, _SZ, ctypes.POINTER(ctypes.c_double),
@@ -253,3 +261,53 @@ def attn_bwd(q, k, v, o, dout, lse, position_ids=None, scale=None, dq=None, dk=N
                            _dev(dv, "dv"), N, Hq, Hkv, D, scale, _dtype_code(q), ws.data_ptr(), wsb,
                            _stream(q.device)))
     return dq, dk, dv
+
+
+def rank_workspace_bytes(N, Hq, Hkv, D, P, chunks, dtype, for_bwd):
+    code = UL_BF16 if dtype == torch.bfloat16 else UL_F32 if dtype == torch.float32 else -1
+    return load().ul_rank_workspace_bytes(N, Hq, Hkv, D, P, chunks, code, 1 if for_bwd else 0)
+
+
+def rank_attn_fwd(q_seq, k_seq, v_seq, P, rank, position_ids=None, chunks=1, scale=None, o_seq=None, lse=None,
+                  workspace=None):
+    """Rank's whole forward path (seq->head, attention, head->seq) in `chunks` head chunks.
+
+    Writes the rank's columns of o_seq [N, Hq, D] (allocated with zeros if None) and returns
+    (o_seq, lse [Hq/P, N] fp32)."""
+    lib = load()
+    N, Hq, D = q_seq.shape
+    Hkv = k_seq.shape[1]
+    if k_seq.shape != v_seq.shape or k_seq.dtype != q_seq.dtype or v_seq.dtype != q_seq.dtype:
+        raise ValueError("q_seq, k_seq, v_seq shapes or dtypes disagree")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o_seq = torch.zeros_like(q_seq) if o_seq is None else o_seq
+    if lse is None:
+        lse = torch.empty((Hq // P if P > 0 and Hq % P == 0 else 1, N), dtype=torch.float32, device=q_seq.device)
+    wsb = lib.ul_rank_workspace_bytes(N, Hq, Hkv, D, P, chunks, _dtype_code(q_seq), 0)
+    ws = _workspace(wsb, q_seq.device, workspace)
+    _check(lib.ul_rank_attn_fwd(_dev(q_seq, "q_seq"), _dev(k_seq, "k_seq"), _dev(v_seq, "v_seq"),
+                                _pos_ptr(position_ids, N), _dev(o_seq, "o_seq"), _dev(lse, "lse"), N, Hq, Hkv, D, P,
+                                rank, chunks, scale, _dtype_code(q_seq), ws.data_ptr(), wsb, _stream(q_seq.device)))
+    return o_seq, lse
+
+
+def rank_attn_bwd(q_seq, k_seq, v_seq, o_seq, do_seq, lse, P, rank, position_ids=None, chunks=1, scale=None,
+                  dq_seq=None, dk_seq=None, dv_seq=None, workspace=None):
+    """Rank's whole backward path in `chunks` head chunks; returns fp32 (dq_seq, dk_seq, dv_seq) in sequence
+    layout with the rank's columns written (zero-filled if allocated here)."""
+    lib = load()
+    N, Hq, D = q_seq.shape
+    Hkv = k_seq.shape[1]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    f32 = dict(dtype=torch.float32, device=q_seq.device)
+    dq_seq = torch.zeros((N, Hq, D), **f32) if dq_seq is None else dq_seq
+    dk_seq = torch.zeros((N, Hkv, D), **f32) if dk_seq is None else dk_seq
+    dv_seq = torch.zeros((N, Hkv, D), **f32) if dv_seq is None else dv_seq
+    wsb = lib.ul_rank_workspace_bytes(N, Hq, Hkv, D, P, chunks, _dtype_code(q_seq), 1)
+    ws = _workspace(wsb, q_seq.device, workspace)
+    _check(lib.ul_rank_attn_bwd(_dev(q_seq, "q_seq"), _dev(k_seq, "k_seq"), _dev(v_seq, "v_seq"),
+                                _dev(o_seq, "o_seq"), _dev(do_seq, "do_seq"), _dev(lse, "lse"),
+                                _pos_ptr(position_ids, N), _dev(dq_seq, "dq_seq"), _dev(dk_seq, "dk_seq"),
+                                _dev(dv_seq, "dv_seq"), N, Hq, Hkv, D, P, rank, chunks, scale, _dtype_code(q_seq),
+                                ws.data_ptr(), wsb, _stream(q_seq.device)))
+    return dq_seq, dk_seq, dv_seq

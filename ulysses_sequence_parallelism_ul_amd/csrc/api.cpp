@@ -92,6 +92,84 @@ ul_status check_attn_shapes(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, float
   return UL_OK;
 }
 
+// ---- rank level: the whole per-rank path, optionally in head chunks ----
+
+// How rank `rank`'s heads split into `chunks` chunks of consecutive q heads.
+struct RankPlan {
+  int hq = 0, hkv = 0, G = 0;  // the rank's q heads, KV heads and group size
+  int C = 0, qc = 0, kc = 0;   // chunks, q heads and KV heads per chunk
+  bool kv_shared = false;      // kc = 1 and qc < G: consecutive chunks share one KV head
+  // first rank-local KV head of chunk c
+  int kv0(int c) const { return kv_shared ? (c * qc) / G : c * kc; }
+};
+
+ul_status plan_rank(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t rank, int32_t chunks,
+                    float scale, ul_dtype dt, RankPlan* pl) {
+  if (dt != UL_BF16 && dt != UL_F32) return fail(UL_ERR_UNSUPPORTED, "dtype %d is not UL_F32 or UL_BF16", (int)dt);
+  if (P < 1) return fail(UL_ERR_ARG, "P=%d must be >= 1", P);
+  if (rank < 0 || rank >= P) return fail(UL_ERR_ARG, "rank %d outside [0, %d)", rank, P);
+  if (N < 1) return fail(UL_ERR_ARG, "N=%lld must be >= 1", (long long)N);
+  if (N % P != 0) return fail(UL_ERR_ARG, "sequence length N=%lld is not divisible by P=%d", (long long)N, P);
+  if (Hq < 1 || Hkv < 1 || Hq % P != 0 || Hkv % P != 0)
+    return fail(UL_ERR_ARG, "Hq=%d and Hkv=%d must be positive multiples of P=%d", Hq, Hkv, P);
+  RankPlan r;
+  r.hq = Hq / P;
+  r.hkv = Hkv / P;
+  if (r.hq % r.hkv != 0) return fail(UL_ERR_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  r.G = r.hq / r.hkv;
+  if (chunks < 1 || r.hq % chunks != 0)
+    return fail(UL_ERR_ARG, "chunks=%d must divide the rank's %d query heads", chunks, r.hq);
+  r.C = chunks;
+  r.qc = r.hq / chunks;
+  if (r.qc % r.G == 0) {
+    r.kc = r.qc / r.G;
+  } else if (r.G % r.qc == 0) {
+    r.kc = 1;
+    r.kv_shared = true;
+  } else {
+    return fail(UL_ERR_ARG, "a chunk of %d query heads neither covers whole groups of %d nor divides one", r.qc, r.G);
+  }
+  ul_status st = check_attn_shapes(N, r.qc, r.kc, D, scale, dt);
+  if (st != UL_OK) return st;
+  *pl = r;
+  return UL_OK;
+}
+
+// Workspace of the rank-level calls: the per-chunk attention workspace first
+// (its document bounds serve every chunk), then the chunk buffers.
+struct RankWs {
+  ul::WsLayout att;
+  size_t qh = 0, kh = 0, vh = 0, oh = 0;           // head-layout chunks, input dtype
+  size_t doh = 0, dqh = 0, dkh = 0, dvh = 0;       // bwd: dO chunk (input dtype); dQ, dK, dV chunks (fp32)
+  size_t dkc = 0, dvc = 0;                         // bwd with a shared KV head: this chunk's dK, dV partials
+  size_t total = 0;
+};
+
+RankWs rank_ws(int64_t N, int32_t D, ul_dtype dt, const RankPlan& r, bool for_bwd) {
+  RankWs W;
+  const size_t A = 256, e = (size_t)elem_bytes(dt);
+  W.att = ul::ws_layout(N, r.qc, r.kc, D, dt, for_bwd);
+  size_t off = ul::align_up(W.att.total, A);
+  const size_t q_e = (size_t)N * r.qc * D * e, kv_e = (size_t)N * r.kc * D * e;
+  W.qh = off; off = ul::align_up(off + q_e, A);
+  W.kh = off; off = ul::align_up(off + kv_e, A);
+  W.vh = off; off = ul::align_up(off + kv_e, A);
+  W.oh = off; off = ul::align_up(off + q_e, A);
+  if (for_bwd) {
+    const size_t q_f = (size_t)N * r.qc * D * 4, kv_f = (size_t)N * r.kc * D * 4;
+    W.doh = off; off = ul::align_up(off + q_e, A);
+    W.dqh = off; off = ul::align_up(off + q_f, A);
+    W.dkh = off; off = ul::align_up(off + kv_f, A);
+    W.dvh = off; off = ul::align_up(off + kv_f, A);
+    if (r.kv_shared && r.C > 1) {
+      W.dkc = off; off = ul::align_up(off + kv_f, A);
+      W.dvc = off; off = ul::align_up(off + kv_f, A);
+    }
+  }
+  W.total = off;
+  return W;
+}
+
 }  // namespace
 
 namespace ul {
@@ -248,6 +326,151 @@ ul_status ul_attn_bwd(const void* q, const void* k, const void* v, const void* o
                                   D, scale, s);
   if (err == hipErrorNotSupported) return fail(UL_ERR_UNSUPPORTED, "attn_bwd: this configuration is not built");
   return hip_status(err, "attn_bwd launch");
+}
+
+size_t ul_rank_workspace_bytes(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t chunks, ul_dtype dt,
+                               int32_t for_bwd) {
+  std::string saved = g_err;
+  RankPlan r;
+  ul_status st = plan_rank(N, Hq, Hkv, D, P, 0, chunks, 1.0f, dt, &r);
+  g_err = saved;
+  if (st != UL_OK) return 0;
+  return rank_ws(N, D, dt, r, for_bwd != 0).total;
+}
+
+ul_status ul_rank_attn_fwd(const void* q_seq, const void* k_seq, const void* v_seq, const int32_t* position_ids,
+                           void* o_seq, float* lse, int64_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                           int32_t rank, int32_t chunks, float scale, ul_dtype dt, void* ws, size_t ws_bytes,
+                           void* stream) {
+  RankPlan r;
+  ul_status st = plan_rank(N, Hq, Hkv, D, P, rank, chunks, scale, dt, &r);
+  if (st != UL_OK) return st;
+  const size_t e = (size_t)elem_bytes(dt);
+  const RankWs W = rank_ws(N, D, dt, r, false);
+  const size_t nq = (size_t)N * Hq * D * e, nkv = (size_t)N * Hkv * D * e;
+  Buf bufs[6] = {{q_seq, nq, "q_seq"}, {k_seq, nkv, "k_seq"}, {v_seq, nkv, "v_seq"}, {o_seq, nq, "o_seq"},
+                 {lse, (size_t)r.hq * N * 4, "lse"}, {ws, W.total, "ws"}};
+  for (int i = 0; i < 6; ++i) {
+    if (bufs[i].p == nullptr) return fail(UL_ERR_ARG, "%s is NULL", bufs[i].name);
+    if (!aligned(bufs[i].p, 16)) return fail(UL_ERR_ARG, "%s is not 16-byte aligned", bufs[i].name);
+  }
+  for (int i = 3; i < 6; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (i != j && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
+        return fail(UL_ERR_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
+  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  if (ws_bytes < W.total) return fail(UL_ERR_ARG, "workspace of %zu bytes is smaller than %zu", ws_bytes, W.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  int32_t* ds = reinterpret_cast<int32_t*>(w + W.att.doc_start);
+  int32_t* de = reinterpret_cast<int32_t*>(w + W.att.doc_end);
+  hipError_t err = ul::launch_doc_bounds(position_ids, ds, de, reinterpret_cast<int32_t*>(w + W.att.scan), (int)N, s);
+  for (int c = 0; c < r.C && err == hipSuccess; ++c) {
+    const int qpart = r.hq / r.qc * P, qidx = rank * r.C + c;  // chunk c = head block qidx of Hq / qc
+    const int kvpart = Hkv / r.kc, kvidx = (rank * r.hkv + r.kv0(c)) / r.kc;
+    if (c == 0 || r.kv0(c) != r.kv0(c - 1)) {
+      err = ul::launch_relayout(k_seq, w + W.kh, N, Hkv, D, kvpart, kvidx, (int)e, true, s);
+      if (err == hipSuccess) err = ul::launch_relayout(v_seq, w + W.vh, N, Hkv, D, kvpart, kvidx, (int)e, true, s);
+    }
+    if (err == hipSuccess) err = ul::launch_relayout(q_seq, w + W.qh, N, Hq, D, qpart, qidx, (int)e, true, s);
+    float* lse_c = lse + (size_t)c * r.qc * N;
+    if (err == hipSuccess) {
+      if (dt == UL_BF16)
+        err = ul::launch_attn_fwd_bf16(reinterpret_cast<const ul::bf16*>(w + W.qh),
+                                       reinterpret_cast<const ul::bf16*>(w + W.kh),
+                                       reinterpret_cast<const ul::bf16*>(w + W.vh), ds,
+                                       reinterpret_cast<ul::bf16*>(w + W.oh), lse_c,
+                                       reinterpret_cast<ul::bf16*>(w + W.att.vt), (int)N, r.qc, r.kc, D, scale, s);
+      else
+        err = ul::launch_attn_fwd_f32(reinterpret_cast<const float*>(w + W.qh),
+                                      reinterpret_cast<const float*>(w + W.kh),
+                                      reinterpret_cast<const float*>(w + W.vh), ds, reinterpret_cast<float*>(w + W.oh),
+                                      lse_c, (int)N, r.qc, r.kc, D, scale, s);
+    }
+    if (err == hipSuccess) err = ul::launch_relayout(w + W.oh, o_seq, N, Hq, D, qpart, qidx, (int)e, false, s);
+  }
+  return hip_status(err, "rank_attn_fwd launch");
+}
+
+ul_status ul_rank_attn_bwd(const void* q_seq, const void* k_seq, const void* v_seq, const void* o_seq,
+                           const void* do_seq, const float* lse, const int32_t* position_ids, float* dq_seq,
+                           float* dk_seq, float* dv_seq, int64_t N, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                           int32_t rank, int32_t chunks, float scale, ul_dtype dt, void* ws, size_t ws_bytes,
+                           void* stream) {
+  RankPlan r;
+  ul_status st = plan_rank(N, Hq, Hkv, D, P, rank, chunks, scale, dt, &r);
+  if (st != UL_OK) return st;
+  const size_t e = (size_t)elem_bytes(dt);
+  const RankWs W = rank_ws(N, D, dt, r, true);
+  const size_t nq = (size_t)N * Hq * D * e, nkv = (size_t)N * Hkv * D * e;
+  const size_t fq = (size_t)N * Hq * D * 4, fkv = (size_t)N * Hkv * D * 4;
+  Buf bufs[10] = {{q_seq, nq, "q_seq"}, {k_seq, nkv, "k_seq"}, {v_seq, nkv, "v_seq"}, {o_seq, nq, "o_seq"},
+                  {do_seq, nq, "do_seq"}, {lse, (size_t)r.hq * N * 4, "lse"}, {dq_seq, fq, "dq_seq"},
+                  {dk_seq, fkv, "dk_seq"}, {dv_seq, fkv, "dv_seq"}, {ws, W.total, "ws"}};
+  for (int i = 0; i < 10; ++i) {
+    if (bufs[i].p == nullptr) return fail(UL_ERR_ARG, "%s is NULL", bufs[i].name);
+    if (!aligned(bufs[i].p, 16)) return fail(UL_ERR_ARG, "%s is not 16-byte aligned", bufs[i].name);
+  }
+  for (int i = 6; i < 10; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (i != j && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
+        return fail(UL_ERR_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
+  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  if (ws_bytes < W.total) return fail(UL_ERR_ARG, "workspace of %zu bytes is smaller than %zu", ws_bytes, W.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  int32_t* ds = reinterpret_cast<int32_t*>(w + W.att.doc_start);
+  int32_t* de = reinterpret_cast<int32_t*>(w + W.att.doc_end);
+  float* delta = reinterpret_cast<float*>(w + W.att.delta);
+  float* dqh = reinterpret_cast<float*>(w + W.dqh);
+  float* dkh = reinterpret_cast<float*>(w + W.dkh);
+  float* dvh = reinterpret_cast<float*>(w + W.dvh);
+  const int64_t nkv_chunk = N * r.kc * D;
+  hipError_t err = ul::launch_doc_bounds(position_ids, ds, de, reinterpret_cast<int32_t*>(w + W.att.scan), (int)N, s);
+  for (int c = 0; c < r.C && err == hipSuccess; ++c) {
+    const int qpart = r.hq / r.qc * P, qidx = rank * r.C + c;
+    const int kvpart = Hkv / r.kc, kvidx = (rank * r.hkv + r.kv0(c)) / r.kc;
+    const bool first_of_kv = c == 0 || r.kv0(c) != r.kv0(c - 1);
+    const bool last_of_kv = c == r.C - 1 || r.kv0(c + 1) != r.kv0(c);
+    if (first_of_kv) {
+      err = ul::launch_relayout(k_seq, w + W.kh, N, Hkv, D, kvpart, kvidx, (int)e, true, s);
+      if (err == hipSuccess) err = ul::launch_relayout(v_seq, w + W.vh, N, Hkv, D, kvpart, kvidx, (int)e, true, s);
+    }
+    if (err == hipSuccess) err = ul::launch_relayout(q_seq, w + W.qh, N, Hq, D, qpart, qidx, (int)e, true, s);
+    if (err == hipSuccess) err = ul::launch_relayout(o_seq, w + W.oh, N, Hq, D, qpart, qidx, (int)e, true, s);
+    if (err == hipSuccess) err = ul::launch_relayout(do_seq, w + W.doh, N, Hq, D, qpart, qidx, (int)e, true, s);
+    // the first chunk of a KV head writes its dK / dV accumulators, later chunks their own partials
+    float* dk_out = first_of_kv ? dkh : reinterpret_cast<float*>(w + W.dkc);
+    float* dv_out = first_of_kv ? dvh : reinterpret_cast<float*>(w + W.dvc);
+    const float* lse_c = lse + (size_t)c * r.qc * N;
+    if (err == hipSuccess) {
+      if (dt == UL_BF16)
+        err = ul::launch_attn_bwd_bf16(
+            reinterpret_cast<const ul::bf16*>(w + W.qh), reinterpret_cast<const ul::bf16*>(w + W.kh),
+            reinterpret_cast<const ul::bf16*>(w + W.vh), reinterpret_cast<const ul::bf16*>(w + W.oh),
+            reinterpret_cast<const ul::bf16*>(w + W.doh), lse_c, ds, de, dqh, dk_out, dv_out, delta, (int)N, r.qc,
+            r.kc, D, scale, s);
+      else
+        err = ul::launch_attn_bwd_f32(
+            reinterpret_cast<const float*>(w + W.qh), reinterpret_cast<const float*>(w + W.kh),
+            reinterpret_cast<const float*>(w + W.vh), reinterpret_cast<const float*>(w + W.oh),
+            reinterpret_cast<const float*>(w + W.doh), lse_c, ds, de, dqh, dk_out, dv_out, delta, (int)N, r.qc,
+            r.kc, D, scale, s);
+    }
+    if (err == hipSuccess && !first_of_kv) {
+      err = ul::launch_add_f32(dkh, dk_out, nkv_chunk, s);
+      if (err == hipSuccess) err = ul::launch_add_f32(dvh, dv_out, nkv_chunk, s);
+    }
+    if (err == hipSuccess) err = ul::launch_relayout(dqh, dq_seq, N, Hq, D, qpart, qidx, 4, false, s);
+    if (err == hipSuccess && last_of_kv) {
+      err = ul::launch_relayout(dkh, dk_seq, N, Hkv, D, kvpart, kvidx, 4, false, s);
+      if (err == hipSuccess) err = ul::launch_relayout(dvh, dv_seq, N, Hkv, D, kvpart, kvidx, 4, false, s);
+    }
+  }
+  if (err == hipErrorNotSupported) return fail(UL_ERR_UNSUPPORTED, "rank_attn_bwd: this configuration is not built");
+  return hip_status(err, "rank_attn_bwd launch");
 }
 
 }  // extern "C"

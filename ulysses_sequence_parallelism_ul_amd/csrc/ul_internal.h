@@ -62,6 +62,8 @@ hipError_t launch_doc_bounds(const int32_t* pos, int32_t* doc_start, int32_t* do
 // [N][H][D] tensor) -> blocked transpose [Hkv][ceil(ncols / kTB)][D][kTB], zero-padded.
 hipError_t launch_transpose_blocked(const bf16* src, bf16* dst, int64_t ncols, int H, int Hkv, int lgG, int D,
                                     hipStream_t s);
+// dst[i] += src[i] for n floats (n a multiple of 4, 16-byte aligned buffers).
+hipError_t launch_add_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 hipError_t launch_attn_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* doc_start,
                                 bf16* o, float* lse, bf16* vt_ws, int N, int Hq, int Hkv, int D,
                                 float scale, hipStream_t s);
