@@ -197,6 +197,33 @@ ul_status ul_rank_attn_bwd(const void *q_seq, const void *k_seq, const void *v_s
                            ul_dtype dt, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The projections on either side of the path, for one rank's own token shard
+ * (page "Hugging Face并行加速", nmedialink.com, section "Ulysses的工作原理":
+ * step 2, each GPU projects its shard into Q, K and V; step 6, the output
+ * projection after the return exchange).  bf16 operands, fp32 accumulation on
+ * MFMA, bf16 results; dt must be UL_BF16.
+ * ul_qkv_proj_pack: x [M][hidden] (the shard's M tokens) times
+ *   w_qkv [(Hq + 2 Hkv) D][hidden] (one row per output feature: rows
+ *   [0, Hq D) project Q, the next Hkv D rows K, the last Hkv D rows V; head h
+ *   of a tensor is its D consecutive features).  The results go straight into
+ *   the all-to-all send blocks instead of [M][H][D]:
+ *   q_send [P][M][Hq/P][D] and k_send / v_send [P][M][Hkv/P][D], block j
+ *   holding heads [j H/P, (j+1) H/P) for rank j (the exchange then delivers
+ *   rank j the blocks j of every shard, i.e. ul_seq_to_head's x_head).
+ *   hidden must be a multiple of 64; Hq and Hkv multiples of P.
+ * ul_out_proj: o_seq [M][HqD] (the attention output back in the sequence
+ *   layout, read as is) times w_o [hidden][HqD] -> y [M][hidden];
+ *   HqD must be a multiple of 64.
+ * Errors: UL_ERR_ARG for the shape rules, null or misaligned pointers, outputs
+ * overlapping anything; UL_ERR_UNSUPPORTED for dt != UL_BF16.  No workspace.
+ */
+ul_status ul_qkv_proj_pack(const void *x, const void *w_qkv, void *q_send, void *k_send, void *v_send,
+                           int64_t M, int32_t hidden, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                           ul_dtype dt, void *stream);
+ul_status ul_out_proj(const void *o_seq, const void *w_o, void *y, int64_t M, int32_t hidden, int32_t HqD,
+                      ul_dtype dt, void *stream);
+
+/*
  * Optional per-kernel timing for benchmarks.  While enabled, every kernel the
  * library launches is bracketed by two hipEvents recorded on the kernel's own
  * stream; elapsed times are summed per kernel name.  Off by default.

@@ -16,6 +16,8 @@ boolean mask:
 * ``docs``      - document ids and per-row document bounds from position ids.
 * ``attention`` - causal, packed-document, grouped-query softmax attention,
   forward and backward, plus sampled-row forms for very long sequences.
+* ``projection`` - the QKV projection of one shard into the send blocks of
+  the first exchange, and the output projection.
 
 Page citations name the page by its title and host and then the section.
 The pages are:
@@ -28,7 +30,8 @@ The pages are:
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, finite differences, invariants that the
 pages fix, and a library routine (torch CPU scaled-dot-product attention) on
-single-document cases.
+single-document cases; the projections against per-element sums and the
+exchange oracle.
 """
 
 from .relayout import (
@@ -49,6 +52,7 @@ from .attention import (
     attn_fwd_per_document,
     attn_bwd_per_document,
 )
+from .projection import linear, split_heads, send_blocks, qkv_proj_pack, out_proj
 
 __all__ = [
     "seq_to_head",
@@ -66,4 +70,9 @@ __all__ = [
     "attn_bwd_dkdv_rows",
     "attn_fwd_per_document",
     "attn_bwd_per_document",
+    "linear",
+    "split_heads",
+    "send_blocks",
+    "qkv_proj_pack",
+    "out_proj",
 ]

@@ -167,3 +167,20 @@ def test_rank_workspace_and_rejections():
     assert bwd(chunks=8) == ul.UL_ERR_ARG
     assert bwd(dk=G_) == ul.UL_ERR_ARG  # dk overlaps dq
     assert bwd(wsb=64) == ul.UL_ERR_ARG
+
+
+def test_projection_rejections_cpu():
+    lib = ul.load()
+
+    def qkv(M=16, hidden=128, Hq=4, Hkv=2, D=64, P=2, dt=ul.UL_BF16, x=A, q=C):
+        return lib.ul_qkv_proj_pack(x, B, q, D_, E, M, hidden, Hq, Hkv, D, P, dt, None)
+
+    assert qkv(hidden=100) == ul.UL_ERR_ARG
+    assert qkv(Hkv=3) == ul.UL_ERR_ARG      # not a multiple of P
+    assert qkv(M=0) == ul.UL_ERR_ARG
+    assert qkv(dt=ul.UL_F32) == ul.UL_ERR_UNSUPPORTED
+    assert qkv(x=None) == ul.UL_ERR_ARG
+    assert qkv(q=A) == ul.UL_ERR_ARG        # q_send overlaps x
+    assert lib.ul_out_proj(A, B, C, 16, 64, 96, ul.UL_BF16, None) == ul.UL_ERR_ARG   # HqD % 64
+    assert lib.ul_out_proj(A, B, A, 16, 64, 128, ul.UL_BF16, None) == ul.UL_ERR_ARG  # y overlaps o_seq
+    assert lib.ul_out_proj(A, B, C, 16, 64, 128, ul.UL_F32, None) == ul.UL_ERR_UNSUPPORTED

@@ -29,6 +29,8 @@ __all__ = [
     "rank_workspace_bytes",
     "rank_attn_fwd",
     "rank_attn_bwd",
+    "qkv_proj_pack",
+    "out_proj",
     "timing_enable",
     "timing_reset",
     "timing_read",
@@ -67,6 +69,8 @@ SIGNATURES = {
                                 _P]),
     "ul_rank_attn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                 _I32, _P, _SZ, _P]),
+    "ul_qkv_proj_pack": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+    "ul_out_proj": (_I32, [_P, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "ul_timing_enable": (_I32, [_I32]),
     "ul_timing_reset": (None, []),
     "ul_timing_read": (_I32, [_I32, ctypes.c_char_p, _SZ, ctypes.POINTER(ctypes.c_double),
@@ -311,3 +315,35 @@ def rank_attn_bwd(q_seq, k_seq, v_seq, o_seq, do_seq, lse, P, rank, position_ids
                                 _dev(dv_seq, "dv_seq"), N, Hq, Hkv, D, P, rank, chunks, scale, _dtype_code(q_seq),
                                 ws.data_ptr(), wsb, _stream(q_seq.device)))
     return dq_seq, dk_seq, dv_seq
+
+
+def qkv_proj_pack(x, w_qkv, Hq, Hkv, D, P, q_send=None, k_send=None, v_send=None):
+    """Shard projection x [M, hidden] @ w_qkv^T into the send blocks (q_send [P, M, Hq/P, D], k_send and v_send
+    [P, M, Hkv/P, D]); bf16."""
+    lib = load()
+    M, hidden = x.shape
+    if tuple(w_qkv.shape) != ((Hq + 2 * Hkv) * D, hidden):
+        raise ValueError(f"w_qkv shape {tuple(w_qkv.shape)} is not [(Hq + 2 Hkv) D, hidden]")
+    opt = dict(dtype=x.dtype, device=x.device)
+    if P < 1 or Hq % P or Hkv % P:
+        raise ValueError(f"Hq={Hq} and Hkv={Hkv} must be multiples of P={P}")
+    q_send = torch.empty((P, M, Hq // P, D), **opt) if q_send is None else q_send
+    k_send = torch.empty((P, M, Hkv // P, D), **opt) if k_send is None else k_send
+    v_send = torch.empty((P, M, Hkv // P, D), **opt) if v_send is None else v_send
+    _check(lib.ul_qkv_proj_pack(_dev(x, "x"), _dev(w_qkv, "w_qkv"), _dev(q_send, "q_send"), _dev(k_send, "k_send"),
+                                _dev(v_send, "v_send"), M, hidden, Hq, Hkv, D, P, _dtype_code(x), _stream(x.device)))
+    return q_send, k_send, v_send
+
+
+def out_proj(o_seq, w_o, y=None):
+    """Output projection: o_seq [M, Hq*D] (or [M, Hq, D]) @ w_o^T -> y [M, hidden]; bf16."""
+    lib = load()
+    M = o_seq.shape[0]
+    HqD = o_seq.numel() // M
+    hidden = w_o.shape[0]
+    if tuple(w_o.shape) != (hidden, HqD):
+        raise ValueError(f"w_o shape {tuple(w_o.shape)} is not [hidden, Hq*D={HqD}]")
+    y = torch.empty((M, hidden), dtype=o_seq.dtype, device=o_seq.device) if y is None else y
+    _check(lib.ul_out_proj(_dev(o_seq, "o_seq"), _dev(w_o, "w_o"), _dev(y, "y"), M, hidden, HqD, _dtype_code(o_seq),
+                           _stream(o_seq.device)))
+    return y

@@ -473,4 +473,53 @@ ul_status ul_rank_attn_bwd(const void* q_seq, const void* k_seq, const void* v_s
   return hip_status(err, "rank_attn_bwd launch");
 }
 
+ul_status ul_qkv_proj_pack(const void* x, const void* w_qkv, void* q_send, void* k_send, void* v_send, int64_t M,
+                           int32_t hidden, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, ul_dtype dt,
+                           void* stream) {
+  if (dt != UL_BF16) return fail(UL_ERR_UNSUPPORTED, "the projections take bf16 (dtype %d)", (int)dt);
+  if (M < 1) return fail(UL_ERR_ARG, "M=%lld must be >= 1", (long long)M);
+  if (hidden < 64 || hidden % 64 != 0) return fail(UL_ERR_ARG, "hidden=%d must be a positive multiple of 64", hidden);
+  if (D < 1 || P < 1 || Hq < 1 || Hkv < 1) return fail(UL_ERR_ARG, "D, P, Hq and Hkv must be >= 1");
+  if (Hq % P != 0 || Hkv % P != 0)
+    return fail(UL_ERR_ARG, "Hq=%d and Hkv=%d must be multiples of P=%d", Hq, Hkv, P);
+  const int64_t width = (int64_t)(Hq + 2 * Hkv) * D;
+  if (width > 0x7fffffffLL) return fail(UL_ERR_ARG, "(Hq + 2 Hkv) * D is too large");
+  const size_t xq = (size_t)M * Hq * D * 2, xkv = (size_t)M * Hkv * D * 2;
+  Buf bufs[5] = {{x, (size_t)M * hidden * 2, "x"}, {w_qkv, (size_t)width * hidden * 2, "w_qkv"},
+                 {q_send, xq, "q_send"}, {k_send, xkv, "k_send"}, {v_send, xkv, "v_send"}};
+  for (int i = 0; i < 5; ++i) {
+    if (bufs[i].p == nullptr) return fail(UL_ERR_ARG, "%s is NULL", bufs[i].name);
+    if (!aligned(bufs[i].p, 16)) return fail(UL_ERR_ARG, "%s is not 16-byte aligned", bufs[i].name);
+  }
+  for (int i = 2; i < 5; ++i)
+    for (int j = 0; j < 5; ++j)
+      if (i != j && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
+        return fail(UL_ERR_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
+  return hip_status(ul::launch_qkv_proj_pack(static_cast<const ul::bf16*>(x), static_cast<const ul::bf16*>(w_qkv),
+                                             static_cast<ul::bf16*>(q_send), static_cast<ul::bf16*>(k_send),
+                                             static_cast<ul::bf16*>(v_send), M, hidden, Hq, Hkv, D, P,
+                                             (hipStream_t)stream),
+                    "qkv_proj_pack launch");
+}
+
+ul_status ul_out_proj(const void* o_seq, const void* w_o, void* y, int64_t M, int32_t hidden, int32_t HqD,
+                      ul_dtype dt, void* stream) {
+  if (dt != UL_BF16) return fail(UL_ERR_UNSUPPORTED, "the projections take bf16 (dtype %d)", (int)dt);
+  if (M < 1) return fail(UL_ERR_ARG, "M=%lld must be >= 1", (long long)M);
+  if (hidden < 1) return fail(UL_ERR_ARG, "hidden=%d must be >= 1", hidden);
+  if (HqD < 64 || HqD % 64 != 0) return fail(UL_ERR_ARG, "Hq*D=%d must be a positive multiple of 64", HqD);
+  Buf bufs[3] = {{o_seq, (size_t)M * HqD * 2, "o_seq"}, {w_o, (size_t)hidden * HqD * 2, "w_o"},
+                 {y, (size_t)M * hidden * 2, "y"}};
+  for (int i = 0; i < 3; ++i) {
+    if (bufs[i].p == nullptr) return fail(UL_ERR_ARG, "%s is NULL", bufs[i].name);
+    if (!aligned(bufs[i].p, 16)) return fail(UL_ERR_ARG, "%s is not 16-byte aligned", bufs[i].name);
+  }
+  for (int j = 0; j < 2; ++j)
+    if (overlap(bufs[2].p, bufs[2].n, bufs[j].p, bufs[j].n))
+      return fail(UL_ERR_ARG, "y and %s overlap", bufs[j].name);
+  return hip_status(ul::launch_out_proj(static_cast<const ul::bf16*>(o_seq), static_cast<const ul::bf16*>(w_o),
+                                        static_cast<ul::bf16*>(y), M, hidden, HqD, (hipStream_t)stream),
+                    "out_proj launch");
+}
+
 }  // extern "C"

@@ -62,6 +62,14 @@ hipError_t launch_doc_bounds(const int32_t* pos, int32_t* doc_start, int32_t* do
 // [N][H][D] tensor) -> blocked transpose [Hkv][ceil(ncols / kTB)][D][kTB], zero-padded.
 hipError_t launch_transpose_blocked(const bf16* src, bf16* dst, int64_t ncols, int H, int Hkv, int lgG, int D,
                                     hipStream_t s);
+// Projections (bf16 NT GEMM, fp32 accumulation): x [M][hidden] times w_qkv
+// [(Hq + 2 Hkv) D][hidden] into the send blocks q_send [P][M][Hq/P][D],
+// k_send / v_send [P][M][Hkv/P][D]; o_seq [M][HqD] times w_o [hidden][HqD]
+// into y [M][hidden].  K (hidden, HqD) must be a multiple of 64.
+hipError_t launch_qkv_proj_pack(const bf16* x, const bf16* w_qkv, bf16* q_send, bf16* k_send, bf16* v_send,
+                                int64_t M, int hidden, int Hq, int Hkv, int D, int P, hipStream_t s);
+hipError_t launch_out_proj(const bf16* o_seq, const bf16* w_o, bf16* y, int64_t M, int hidden, int HqD,
+                           hipStream_t s);
 // dst[i] += src[i] for n floats (n a multiple of 4, 16-byte aligned buffers).
 hipError_t launch_add_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 hipError_t launch_attn_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* doc_start,
