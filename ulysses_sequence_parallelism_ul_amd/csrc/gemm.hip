@@ -18,8 +18,8 @@
 // stages of 64 double-buffered in LDS (rows of 128 bytes, 16-byte chunks XOR
 // swizzled by row so 32 rows read at one chunk hit distinct banks), tiles
 // staged through registers one stage ahead.  Work-groups are mapped so each
-// XCD walks all column tiles of one row tile before the next: the 2 MiB row
-// tile of A stays in that XCD's L2 while the weights are shared by everyone.
+// XCD runs groups of 8 row tiles x 4 column tiles together, sharing every K
+// stage's slices of A and B through its L2.
 #include "ul_internal.h"
 
 namespace ul {
@@ -33,6 +33,7 @@ constexpr int kStage = 2 * kTileBytes;              // A tile + B tile
 constexpr int kChunksPerTile = kTileBytes / 16;     // 2048
 constexpr int kLoadsPerThread = kChunksPerTile / kThreads;  // 4 per operand
 constexpr int kXcds = 8;
+constexpr int kGR = 8, kGC = 4;  // tile group per XCD: 8 row tiles x 4 column tiles
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); }
 
@@ -76,13 +77,16 @@ gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int6
                     int n_row_tiles, int n_col_tiles, Epi epi) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
-  // XCD-aware tile order: work-group b runs on XCD b % 8; on each XCD consecutive
-  // work-groups take consecutive column tiles of the same row tile.
+  // XCD-aware tile order: work-group b runs on XCD b % 8; the 32 consecutive
+  // work-groups of one XCD form a group of 8 row tiles x 4 column tiles, whose
+  // A and B slices of each K stage are shared through that XCD's L2.
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds, local = bid / kXcds;
-  const int rt = (local / n_col_tiles) * kXcds + xcd;
-  const int ct = local % n_col_tiles;
-  if (rt >= n_row_tiles) return;
+  const int grp = (local / (kGR * kGC)) * kXcds + xcd, within = local % (kGR * kGC);
+  const int ncg = (n_col_tiles + kGC - 1) / kGC;
+  const int rt = (grp / ncg) * kGR + within / kGC;
+  const int ct = (grp % ncg) * kGC + within % kGC;
+  if (rt >= n_row_tiles || ct >= n_col_tiles) return;
   const int64_t m0 = (int64_t)rt * kBM;
   const int n0 = ct * kBN;
   const int wm = w >> 2, wn = w & 3;  // wave grid 2 x 4: 128 rows x 64 columns each
@@ -179,8 +183,8 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, int64_t M, int Nc, int K, c
   if (M < 1 || Nc < 1 || K < kBK || K % kBK != 0) return hipErrorInvalidValue;
   const int64_t nrt = (M + kBM - 1) / kBM;
   const int nct = (Nc + kBN - 1) / kBN;
-  const int64_t nrt_pad = (nrt + kXcds - 1) / kXcds * kXcds;
-  const int64_t blocks = nrt_pad * nct;
+  const int64_t ngroups = ((nrt + kGR - 1) / kGR) * ((nct + kGC - 1) / kGC);
+  const int64_t blocks = (ngroups + kXcds - 1) / kXcds * kXcds * (kGR * kGC);
   if (nrt > 0x7fffffffLL || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   TimedLaunch timer(name, s);
   hipLaunchKernelGGL(gemm_nt_bf16_kernel<Epi>, dim3((unsigned)blocks), dim3(kThreads), 0, s, A, B, M, Nc, K,
