@@ -18,6 +18,9 @@ boolean mask:
   forward and backward, plus sampled-row forms for very long sequences.
 * ``projection`` - the QKV projection of one shard into the send blocks of
   the first exchange, and the output projection.
+* ``loss``      - next-token targets of a packed sequence, per-token cross
+  entropy of a shard, its token-weighted combination over ranks and the
+  gradient of that loss.
 
 Page citations name the page by its title and host and then the section.
 The pages are:
@@ -31,7 +34,9 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, finite differences, invariants that the
 pages fix, and a library routine (torch CPU scaled-dot-product attention) on
 single-document cases; the projections against per-element sums and the
-exchange oracle.
+exchange oracle; the loss against closed forms, direct per-element sums,
+torch CPU cross entropy, finite differences and the invariance of the
+token-weighted loss to the rank count.
 """
 
 from .relayout import (
@@ -53,6 +58,7 @@ from .attention import (
     attn_bwd_per_document,
 )
 from .projection import linear, split_heads, send_blocks, qkv_proj_pack, out_proj
+from .loss import IGNORE_INDEX, shift_labels, token_ce, valid_count, shard_partial, combine, ce_grad, sp_loss
 
 __all__ = [
     "seq_to_head",
@@ -75,4 +81,12 @@ __all__ = [
     "send_blocks",
     "qkv_proj_pack",
     "out_proj",
+    "IGNORE_INDEX",
+    "shift_labels",
+    "token_ce",
+    "valid_count",
+    "shard_partial",
+    "combine",
+    "ce_grad",
+    "sp_loss",
 ]
