@@ -266,6 +266,17 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
       const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vl + ks * 32);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, dp, 0, 0, 0);
     }
+    // schedule: the operand reads run three MFMAs ahead of the S and dP MFMAs;
+    // the fence keeps the softmax's LDS reads out of this phase (hoisted, they
+    // hold registers the read-ahead needs)
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int j = 0; j < 2 * (D / 16) - 3; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // register i holds query column qh*32 + (i>>3)*16 + g*8 + (i&7) of the tile
     f32x16 pr, dsr;
 #pragma unroll
