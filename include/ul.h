@@ -224,6 +224,59 @@ ul_status ul_out_proj(const void *o_seq, const void *w_o, void *y, int64_t M, in
                       ul_dtype dt, void *stream);
 
 /*
+ * Token-weighted loss of a sequence-sharded step.  The data loader shards the
+ * sequence and every rank computes the loss of its own shard (page "Ulysses
+ * 序列並行：百萬 Token 上下文訓練", setupai.cc, section "增強重點摘要"); the
+ * ranks' losses are weighted by their numbers of valid tokens (page "Ulysses
+ * verteilt Millionen-Token-Kontexte auf mehrere GPUs", dailytechsnack.ch,
+ * section "Integration in den Hugging-Face-Stack").  The loss is next-token
+ * cross entropy.  On P GPUs the ranks' counts, and later their loss sums, are
+ * all-reduced; ul_loss_combine is the arithmetic after that all-reduce, with
+ * the P partials in one device array.  All pointers are device pointers.
+ *
+ * ul_shift_labels: labels [N] int32 of the whole packed sequence (a value equal
+ *   to ignore_index marks a token that is not trained on) and position_ids [N]
+ *   int32 or NULL (one document) -> shift_labels [N] int32 with
+ *   shift_labels[t] = labels[t + 1] when t + 1 < N and position_ids[t + 1] != 0,
+ *   else ignore_index.  Run it before sharding: the last target of a shard is
+ *   the first label of the next shard.  shift_labels must not overlap the
+ *   inputs.
+ * ul_ce_count: count[0] (int64) = number of labels[0..T) != ignore_index; the
+ *   global count is known from the labels alone, before any logits exist.
+ * ul_loss_combine: counts [P] int64 and loss_sums [P] double (may be NULL) ->
+ *   total_count[0] = sum of counts (if total_count is not NULL) and
+ *   loss[0] = sum(loss_sums) / total_count, or 0 when no token is valid (if
+ *   loss is not NULL; it needs loss_sums).  Fixed summation order.
+ * ul_cross_entropy: one shard's logits [T][V] (dtype dt, row-major) and their
+ *   targets labels [T] int32 (from ul_shift_labels) -> loss_tok [T] float,
+ *   the natural-log cross entropy ln(sum_v exp(x_tv)) - x_t,y_t per token (0
+ *   for ignored tokens, NaN for a label outside [0, V) that is not
+ *   ignore_index), and loss_sum[0] (double) = sum of loss_tok, fixed order.
+ *   When dlogits is not NULL it also writes, in dtype dt, the gradient of
+ *   dloss * (token-weighted loss) with respect to this shard's logits:
+ *   dloss / total_count[0] * (softmax(x_t)[v] - [v == y_t]) for valid tokens,
+ *   0 for ignored tokens and when total_count[0] is 0.  total_count (int64,
+ *   e.g. ul_loss_combine over the ranks' ul_ce_count) is required then.
+ *   dlogits may equal logits (the gradient overwrites the logits in place);
+ *   any other overlap is an error.  fp32 arithmetic; each row is read from
+ *   HBM once when V <= 163840 (bf16) or 81920 (fp32), else twice.
+ * Errors: UL_ERR_ARG for N, T, V or P < 1, T or V >= 2^31, null or misaligned
+ * pointers (logits and dlogits 16 bytes, doubles and int64 8, others 4),
+ * overlapping outputs, a non-finite dloss; UL_ERR_UNSUPPORTED for a dtype
+ * other than UL_F32 / UL_BF16 or a row of V elements that is not a multiple
+ * of 16 bytes (V % 8 for bf16, V % 4 for fp32).  All checks run before
+ * anything is enqueued.
+ */
+ul_status ul_shift_labels(const int32_t *labels, const int32_t *position_ids, int32_t *shift_labels, int64_t N,
+                          int32_t ignore_index, void *stream);
+ul_status ul_ce_count(const int32_t *labels, int64_t T, int32_t ignore_index, int64_t *count, void *stream);
+ul_status ul_loss_combine(const double *loss_sums, const int64_t *counts, int32_t P, int64_t *total_count,
+                          double *loss, void *stream);
+ul_status ul_cross_entropy(const void *logits, const int32_t *labels, float *loss_tok, double *loss_sum,
+                           void *dlogits, const int64_t *total_count, float dloss, int64_t T, int32_t V,
+                           int32_t ignore_index, ul_dtype dt, void *stream);
+
+/*
  * Optional per-kernel timing for benchmarks.  While enabled, every kernel the
  * library launches is bracketed by two hipEvents recorded on the kernel's own
  * stream; elapsed times are summed per kernel name.  Off by default.

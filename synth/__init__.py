@@ -113,3 +113,25 @@ def random_positions(N, seed, max_docs=8, min_len=1):
     bounds = [0] + [int(c) for c in cuts] + [N]
     lengths = [b - a for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
     return position_ids_from_lengths(lengths)
+
+
+def token_labels(N, V, seed, frac_ignored=0.1, ignore_index=-100):
+    """int32 token ids uniform in [0, V) with a fraction set to the ignore index (untrained tokens)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 50]))
+    y = rng.integers(0, V, size=N, dtype=np.int64)
+    y[rng.random(N) < frac_ignored] = ignore_index
+    return y.astype(np.int32)
+
+
+def device_logits(T, V, seed, device, dtype, std=3.0, rows_per_draw=2048):
+    """Logits [T, V] ~ N(0, std^2), drawn on the device in row blocks (no fp32 copy of the whole tensor)."""
+    import torch
+
+    out = torch.empty((T, V), dtype=dtype, device=device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1000003 + 60)
+    for r0 in range(0, T, rows_per_draw):
+        r1 = min(T, r0 + rows_per_draw)
+        blk = torch.randn((r1 - r0, V), generator=g, device=device, dtype=torch.float32)
+        out[r0:r1] = (blk * std).to(dtype)
+    return out

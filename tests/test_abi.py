@@ -184,3 +184,46 @@ def test_projection_rejections_cpu():
     assert lib.ul_out_proj(A, B, C, 16, 64, 96, ul.UL_BF16, None) == ul.UL_ERR_ARG   # HqD % 64
     assert lib.ul_out_proj(A, B, A, 16, 64, 128, ul.UL_BF16, None) == ul.UL_ERR_ARG  # y overlaps o_seq
     assert lib.ul_out_proj(A, B, C, 16, 64, 128, ul.UL_F32, None) == ul.UL_ERR_UNSUPPORTED
+
+
+def test_loss_rejections_cpu():
+    lib = ul.load()
+    ign = ul.IGNORE_INDEX
+    # shift labels: N, NULL, overlap, alignment
+    assert lib.ul_shift_labels(A, None, B, 0, ign, None) == ul.UL_ERR_ARG
+    assert lib.ul_shift_labels(None, None, B, 16, ign, None) == ul.UL_ERR_ARG
+    assert lib.ul_shift_labels(A, None, A + 8, 16, ign, None) == ul.UL_ERR_ARG     # out overlaps labels
+    assert lib.ul_shift_labels(A, C, C, 16, ign, None) == ul.UL_ERR_ARG            # out overlaps position_ids
+    assert lib.ul_shift_labels(A, None, B + 2, 16, ign, None) == ul.UL_ERR_ARG     # misaligned
+    # counts
+    assert lib.ul_ce_count(A, 0, ign, B, None) == ul.UL_ERR_ARG
+    assert lib.ul_ce_count(A, 16, ign, A + 8, None) == ul.UL_ERR_ARG              # count overlaps labels
+    assert lib.ul_ce_count(A, 16, ign, B + 4, None) == ul.UL_ERR_ARG              # count misaligned
+    # combine
+    assert lib.ul_loss_combine(A, B, 0, C, D_, None) == ul.UL_ERR_ARG
+    assert lib.ul_loss_combine(A, None, 4, C, D_, None) == ul.UL_ERR_ARG
+    assert lib.ul_loss_combine(A, B, 4, None, None, None) == ul.UL_ERR_ARG          # nothing to write
+    assert lib.ul_loss_combine(None, B, 4, C, D_, None) == ul.UL_ERR_ARG            # loss needs loss_sums
+    assert lib.ul_loss_combine(A, B, 4, B + 8, D_, None) == ul.UL_ERR_ARG           # output overlaps counts
+    assert lib.ul_loss_combine(A, B, 4, C, C, None) == ul.UL_ERR_ARG                # outputs overlap
+
+    # cross entropy
+    def ce(logits=A, labels=B, lt=C, ls=D_, dl=None, tc=None, dloss=1.0, T=8, V=64, dt=ul.UL_BF16):
+        return lib.ul_cross_entropy(logits, labels, lt, ls, dl, tc, dloss, T, V, ign, dt, None)
+
+    assert ce(V=60) == ul.UL_ERR_UNSUPPORTED                  # 120-byte rows
+    assert ce(V=62, dt=ul.UL_F32) == ul.UL_ERR_UNSUPPORTED    # 248-byte rows
+    assert ce(dt=7) == ul.UL_ERR_UNSUPPORTED
+    assert ce(T=0) == ul.UL_ERR_ARG
+    assert ce(T=1 << 31) == ul.UL_ERR_ARG
+    assert ce(V=0) == ul.UL_ERR_ARG
+    assert ce(logits=A + 8) == ul.UL_ERR_ARG                   # logits misaligned
+    assert ce(ls=D_ + 4) == ul.UL_ERR_ARG                      # loss_sum misaligned
+    assert ce(lt=None) == ul.UL_ERR_ARG
+    assert ce(lt=A + 16) == ul.UL_ERR_ARG                      # loss_tok overlaps logits
+    assert ce(ls=C + 8) == ul.UL_ERR_ARG                       # loss_sum overlaps loss_tok
+    assert ce(dl=E) == ul.UL_ERR_ARG                           # gradient without total_count
+    assert ce(dl=A + 16, tc=F) == ul.UL_ERR_ARG                # partial overlap with logits
+    assert ce(dl=E, tc=F, dloss=float("inf")) == ul.UL_ERR_ARG
+    assert ce(dl=E, tc=E + 64) == ul.UL_ERR_ARG                # total_count inside dlogits
+    assert ce(dl=C, tc=F) == ul.UL_ERR_ARG                     # dlogits overlaps loss_tok

@@ -31,6 +31,11 @@ __all__ = [
     "rank_attn_bwd",
     "qkv_proj_pack",
     "out_proj",
+    "IGNORE_INDEX",
+    "shift_labels",
+    "ce_count",
+    "loss_combine",
+    "cross_entropy",
     "timing_enable",
     "timing_reset",
     "timing_read",
@@ -71,6 +76,10 @@ SIGNATURES = {
                                 _I32, _P, _SZ, _P]),
     "ul_qkv_proj_pack": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "ul_out_proj": (_I32, [_P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "ul_shift_labels": (_I32, [_P, _P, _P, _I64, _I32, _P]),
+    "ul_ce_count": (_I32, [_P, _I64, _I32, _P, _P]),
+    "ul_loss_combine": (_I32, [_P, _P, _I32, _P, _P, _P]),
+    "ul_cross_entropy": (_I32, [_P, _P, _P, _P, _P, _P, _F, _I64, _I32, _I32, _I32, _P]),
     "ul_timing_enable": (_I32, [_I32]),
     "ul_timing_reset": (None, []),
     "ul_timing_read": (_I32, [_I32, ctypes.c_char_p, _SZ, ctypes.POINTER(ctypes.c_double),
@@ -347,3 +356,79 @@ def out_proj(o_seq, w_o, y=None):
     _check(lib.ul_out_proj(_dev(o_seq, "o_seq"), _dev(w_o, "w_o"), _dev(y, "y"), M, hidden, HqD, _dtype_code(o_seq),
                            _stream(o_seq.device)))
     return y
+
+
+IGNORE_INDEX = -100
+
+
+def _i32(t, name, n=None):
+    if t.dtype != torch.int32 or (n is not None and t.numel() != n):
+        raise ValueError(f"{name} must be int32" + (f" with {n} elements" if n is not None else ""))
+    return _dev(t, name)
+
+
+def shift_labels(labels, position_ids=None, ignore_index=IGNORE_INDEX, out=None):
+    """Next-token targets [N] int32 of the whole packed sequence (run before sharding)."""
+    lib = load()
+    N = labels.numel()
+    out = torch.empty(N, dtype=torch.int32, device=labels.device) if out is None else out
+    pptr = None if position_ids is None else _i32(position_ids, "position_ids", N)
+    _check(lib.ul_shift_labels(_i32(labels, "labels"), pptr, _i32(out, "out", N), N, ignore_index,
+                               _stream(labels.device)))
+    return out
+
+
+def ce_count(labels, ignore_index=IGNORE_INDEX, count=None):
+    """Number of valid targets of a shard, as a device int64 tensor [1]."""
+    lib = load()
+    count = torch.empty(1, dtype=torch.int64, device=labels.device) if count is None else count
+    _check(lib.ul_ce_count(_i32(labels, "labels"), labels.numel(), ignore_index, _dev(count, "count"),
+                           _stream(labels.device)))
+    return count
+
+
+def loss_combine(counts, loss_sums=None, total_count=None, loss=None):
+    """Token-weighted combination of P ranks' partials: (total_count int64 [1], loss float64 [1] or None)."""
+    lib = load()
+    P = counts.numel()
+    if counts.dtype != torch.int64 or (loss_sums is not None and (loss_sums.dtype != torch.float64
+                                                                  or loss_sums.numel() != P)):
+        raise ValueError("counts must be int64 [P] and loss_sums float64 [P]")
+    dev = counts.device
+    total_count = torch.empty(1, dtype=torch.int64, device=dev) if total_count is None else total_count
+    if loss_sums is not None and loss is None:
+        loss = torch.empty(1, dtype=torch.float64, device=dev)
+    _check(lib.ul_loss_combine(None if loss_sums is None else _dev(loss_sums, "loss_sums"), _dev(counts, "counts"), P,
+                               _dev(total_count, "total_count"), None if loss is None else _dev(loss, "loss"),
+                               _stream(dev)))
+    return total_count, loss
+
+
+def cross_entropy(logits, labels, total_count=None, dloss=1.0, ignore_index=IGNORE_INDEX, grad=False,
+                  in_place=False, loss_tok=None, loss_sum=None, dlogits=None):
+    """Per-token cross entropy of one shard's logits [T, V] (bf16 or fp32) against int32 targets [T].
+
+    Returns (loss_tok float32 [T], loss_sum float64 [1], dlogits or None).  With grad=True, dlogits is the
+    gradient of dloss * (token-weighted loss) for the global valid count total_count (device int64 [1]);
+    in_place=True writes it over the logits."""
+    lib = load()
+    T, V = logits.shape
+    dev = logits.device
+    loss_tok = torch.empty(T, dtype=torch.float32, device=dev) if loss_tok is None else loss_tok
+    loss_sum = torch.empty(1, dtype=torch.float64, device=dev) if loss_sum is None else loss_sum
+    gptr = tcp = None
+    if grad:
+        if total_count is None:
+            raise ValueError("grad=True needs total_count")
+        if in_place:
+            dlogits = logits
+        elif dlogits is None:
+            dlogits = torch.empty_like(logits)
+        gptr = _dev(dlogits, "dlogits")
+        tcp = _dev(total_count, "total_count")
+    else:
+        dlogits = None
+    _check(lib.ul_cross_entropy(_dev(logits, "logits"), _i32(labels, "labels", T), _dev(loss_tok, "loss_tok"),
+                                _dev(loss_sum, "loss_sum"), gptr, tcp, float(dloss), T, V, ignore_index,
+                                _dtype_code(logits), _stream(dev)))
+    return loss_tok, loss_sum, dlogits

@@ -522,4 +522,88 @@ ul_status ul_out_proj(const void* o_seq, const void* w_o, void* y, int64_t M, in
                     "out_proj launch");
 }
 
+ul_status ul_shift_labels(const int32_t* labels, const int32_t* position_ids, int32_t* shift_labels, int64_t N,
+                          int32_t ignore_index, void* stream) {
+  if (N < 1) return fail(UL_ERR_ARG, "N=%lld must be >= 1", (long long)N);
+  const size_t nb = (size_t)N * 4;
+  Buf bufs[3] = {{shift_labels, nb, "shift_labels"}, {labels, nb, "labels"}, {position_ids, nb, "position_ids"}};
+  const int count = position_ids != nullptr ? 3 : 2;
+  ul_status st = check_bufs(bufs, count, 4);
+  if (st != UL_OK) return st;
+  return hip_status(ul::launch_shift_labels(labels, position_ids, shift_labels, N, ignore_index, (hipStream_t)stream),
+                    "shift_labels launch");
+}
+
+ul_status ul_ce_count(const int32_t* labels, int64_t T, int32_t ignore_index, int64_t* count, void* stream) {
+  if (T < 1) return fail(UL_ERR_ARG, "T=%lld must be >= 1", (long long)T);
+  if (labels == nullptr || count == nullptr) return fail(UL_ERR_ARG, "labels and count must not be NULL");
+  if (!aligned(labels, 4) || !aligned(count, 8)) return fail(UL_ERR_ARG, "labels (4) or count (8) misaligned");
+  if (overlap(count, 8, labels, (size_t)T * 4)) return fail(UL_ERR_ARG, "count and labels overlap");
+  return hip_status(ul::launch_count_valid(labels, T, ignore_index, count, (hipStream_t)stream), "ce_count launch");
+}
+
+ul_status ul_loss_combine(const double* loss_sums, const int64_t* counts, int32_t P, int64_t* total_count,
+                          double* loss, void* stream) {
+  if (P < 1) return fail(UL_ERR_ARG, "P=%d must be >= 1", P);
+  if (counts == nullptr) return fail(UL_ERR_ARG, "counts is NULL");
+  if (total_count == nullptr && loss == nullptr) return fail(UL_ERR_ARG, "total_count and loss are both NULL");
+  if (loss != nullptr && loss_sums == nullptr) return fail(UL_ERR_ARG, "loss needs loss_sums");
+  const void* ptrs[4] = {loss_sums, counts, total_count, loss};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] != nullptr && !aligned(ptrs[i], 8)) return fail(UL_ERR_ARG, "a loss_combine pointer is not 8-byte aligned");
+  const size_t pb = (size_t)P * 8;
+  const size_t in_n[2] = {loss_sums ? pb : 0, pb};
+  const void* outs[2] = {total_count, loss};
+  for (int o = 0; o < 2; ++o) {
+    if (outs[o] == nullptr) continue;
+    for (int i = 0; i < 2; ++i)
+      if (ptrs[i] != nullptr && overlap(outs[o], 8, ptrs[i], in_n[i]))
+        return fail(UL_ERR_ARG, "loss_combine outputs overlap its inputs");
+  }
+  if (total_count != nullptr && loss != nullptr && overlap(total_count, 8, loss, 8))
+    return fail(UL_ERR_ARG, "total_count and loss overlap");
+  return hip_status(ul::launch_loss_combine(loss_sums, counts, P, total_count, loss, (hipStream_t)stream),
+                    "loss_combine launch");
+}
+
+ul_status ul_cross_entropy(const void* logits, const int32_t* labels, float* loss_tok, double* loss_sum,
+                           void* dlogits, const int64_t* total_count, float dloss, int64_t T, int32_t V,
+                           int32_t ignore_index, ul_dtype dt, void* stream) {
+  if (dt != UL_BF16 && dt != UL_F32) return fail(UL_ERR_UNSUPPORTED, "dtype %d is not UL_F32 or UL_BF16", (int)dt);
+  if (T < 1 || T > 0x7fffffffLL) return fail(UL_ERR_ARG, "T=%lld must be in [1, 2^31)", (long long)T);
+  if (V < 1) return fail(UL_ERR_ARG, "V=%d must be >= 1", V);
+  const int eb = elem_bytes(dt);
+  if (((int64_t)V * eb) % 16 != 0)
+    return fail(UL_ERR_UNSUPPORTED, "a logits row (V=%d elements of %d bytes) must be a multiple of 16 bytes", V, eb);
+  if (!isfinite(dloss)) return fail(UL_ERR_ARG, "dloss must be finite");
+  const size_t xb = (size_t)T * V * eb;
+  if (logits == nullptr || labels == nullptr || loss_tok == nullptr || loss_sum == nullptr)
+    return fail(UL_ERR_ARG, "logits, labels, loss_tok and loss_sum must not be NULL");
+  if (!aligned(logits, 16)) return fail(UL_ERR_ARG, "logits is not 16-byte aligned");
+  if (!aligned(labels, 4) || !aligned(loss_tok, 4) || !aligned(loss_sum, 8))
+    return fail(UL_ERR_ARG, "labels (4), loss_tok (4) or loss_sum (8) misaligned");
+  Buf outs[2] = {{loss_tok, (size_t)T * 4, "loss_tok"}, {loss_sum, 8, "loss_sum"}};
+  Buf ins[4] = {{logits, xb, "logits"}, {labels, (size_t)T * 4, "labels"}, {total_count, 8, "total_count"},
+                {dlogits, xb, "dlogits"}};
+  int nin = 2;
+  if (dlogits != nullptr) {
+    if (total_count == nullptr) return fail(UL_ERR_ARG, "dlogits needs total_count");
+    if (!aligned(dlogits, 16) || !aligned(total_count, 8))
+      return fail(UL_ERR_ARG, "dlogits (16) or total_count (8) misaligned");
+    if (dlogits != logits && overlap(dlogits, xb, logits, xb))
+      return fail(UL_ERR_ARG, "dlogits overlaps logits without being equal to it");
+    if (overlap(dlogits, xb, labels, (size_t)T * 4) || overlap(dlogits, xb, total_count, 8))
+      return fail(UL_ERR_ARG, "dlogits overlaps labels or total_count");
+    nin = 4;
+  }
+  if (overlap(loss_tok, (size_t)T * 4, loss_sum, 8)) return fail(UL_ERR_ARG, "loss_tok and loss_sum overlap");
+  for (int o = 0; o < 2; ++o)
+    for (int i = 0; i < nin; ++i)
+      if (overlap(outs[o].p, outs[o].n, ins[i].p, ins[i].n))
+        return fail(UL_ERR_ARG, "%s and %s overlap", outs[o].name, ins[i].name);
+  return hip_status(ul::launch_cross_entropy(logits, labels, loss_tok, loss_sum, dlogits, total_count, dloss, T, V,
+                                             ignore_index, dt == UL_BF16, (hipStream_t)stream),
+                    "cross_entropy launch");
+}
+
 }  // extern "C"

@@ -70,6 +70,18 @@ hipError_t launch_qkv_proj_pack(const bf16* x, const bf16* w_qkv, bf16* q_send, 
                                 int64_t M, int hidden, int Hq, int Hkv, int D, int P, hipStream_t s);
 hipError_t launch_out_proj(const bf16* o_seq, const bf16* w_o, bf16* y, int64_t M, int hidden, int HqD,
                            hipStream_t s);
+// Loss of a sharded step: next-token targets, valid counts, per-row cross
+// entropy (+ gradient when dlogits != nullptr) and the combination of ranks.
+hipError_t launch_shift_labels(const int32_t* labels, const int32_t* pos, int32_t* out, int64_t N, int ign,
+                               hipStream_t s);
+hipError_t launch_count_valid(const int32_t* labels, int64_t T, int ign, int64_t* count, hipStream_t s);
+hipError_t launch_cross_entropy(const void* logits, const int32_t* labels, float* loss_tok, double* loss_sum,
+                                void* dlogits, const int64_t* total_count, float dloss, int64_t T, int V, int ign,
+                                bool bf16_in, hipStream_t s);
+hipError_t launch_loss_combine(const double* loss_sums, const int64_t* counts, int P, int64_t* total_out,
+                               double* loss_out, hipStream_t s);
+// Largest vocabulary whose rows the cross-entropy kernel keeps in registers.
+int ce_max_resident_vocab(int elem_bytes);
 // dst[i] += src[i] for n floats (n a multiple of 4, 16-byte aligned buffers).
 hipError_t launch_add_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 hipError_t launch_attn_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* doc_start,
