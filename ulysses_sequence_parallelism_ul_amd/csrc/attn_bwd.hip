@@ -161,6 +161,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   const int kb0 = kblk * C::BNK;
   const int kb_last = min(N - 1, kb0 + C::BNK - 1);
   const int row_end = doc_end[kb_last];
+  const int de0 = doc_end[kb0];  // rows after it belong to later documents than key kb0
   const int tq_lo = (int)(((int64_t)kb0 << lgG) / C::BQ);
   const int tq_hi = (int)((((int64_t)(row_end + 1) << lgG) - 1) / C::BQ);
   const int key = kb0 + kbw * 32 + lc;
@@ -191,16 +192,25 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   u32x4 rq[C::RPT], rdo[C::RPT];
   float a_lse = 0.0f, a_dl = 0.0f;
   int a_row = -1, a_ds = 0;
-  auto gload = [&](int tq) {
+  // A thread loads 16-byte chunk part0 of tile rows r0 + i * RSTEP.  Moving a
+  // tile down by BQ columns (BQ / G whole tokens) moves every source address by
+  // a constant, so only the first tile visited (the one that may run past the
+  // end of the sequence, with clamped columns) computes addresses in full.
+  constexpr int RSTEP = C::kThreads / (D / 8);
+  const int r0 = tid / (D / 8), part0 = tid % (D / 8);
+  const int64_t row_step = (int64_t)RSTEP * Hkv * D, tile_step = (int64_t)C::BQ * Hkv * D;
+  int64_t qoff = col_offset((int64_t)tq_hi * C::BQ + r0, lgG, Hkv, hk, D) + part0 * 8;
+  const int hq_col = (hk << lgG) + (tid & (G - 1));   // query head of aux column tid (tc0 is a multiple of G)
+  int arow = (int)(((int64_t)tq_hi * C::BQ + tid) >> lgG);
+  int64_t acol = (int64_t)tq_hi * C::BQ + tid;
+  auto gload_first = [&](int tq) {
     const int64_t tc0 = (int64_t)tq * C::BQ;
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) {
-      const int ch = tid + i * C::kThreads;
-      const int r = ch / (D / 8), part = ch % (D / 8);
       // columns past the end read the last column instead (their P and dS are
       // masked to zero), so the loads carry no branch
-      const int64_t c = min<int64_t>(tc0 + r, NG - 1);
-      const int64_t off = col_offset(c, lgG, Hkv, hk, D) + part * 8;
+      const int64_t c = min<int64_t>(tc0 + r0 + i * RSTEP, NG - 1);
+      const int64_t off = col_offset(c, lgG, Hkv, hk, D) + part0 * 8;
       rq[i] = *reinterpret_cast<const u32x4*>(q + off);
       rdo[i] = *reinterpret_cast<const u32x4*>(dout + off);
     }
@@ -214,14 +224,29 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
       a_ds = doc_start[row];
     }
   };
+  auto gload_next = [&]() {  // the tile below the one loaded last (always inside the sequence)
+    qoff -= tile_step;
+    arow -= C::BQ >> lgG;
+    acol -= C::BQ;
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) {
+      rq[i] = *reinterpret_cast<const u32x4*>(q + qoff + i * row_step);
+      rdo[i] = *reinterpret_cast<const u32x4*>(dout + qoff + i * row_step);
+    }
+    if (tid < C::BQ) {
+      a_lse = lse[(int64_t)hq_col * N + arow];
+      a_dl = delta[(int64_t)hk * NG + acol];
+      a_row = arow;
+      a_ds = doc_start[arow];
+    }
+  };
   auto lstore = [&](int st) {
     char* b = smem + st * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) {
-      const int ch = tid + i * C::kThreads;
-      const int r = ch / (D / 8), part = ch % (D / 8);
-      *reinterpret_cast<u32x4*>(b + C::Q_OFF + lds_off<D>(tile_row(r), part)) = rq[i];
-      *reinterpret_cast<u32x4*>(b + C::DO_OFF + lds_off<D>(tile_row(r), part)) = rdo[i];
+      const int r = r0 + i * RSTEP;
+      *reinterpret_cast<u32x4*>(b + C::Q_OFF + lds_off<D>(tile_row(r), part0)) = rq[i];
+      *reinterpret_cast<u32x4*>(b + C::DO_OFF + lds_off<D>(tile_row(r), part0)) = rdo[i];
     }
     if (tid < C::BQ) {
       float* af = reinterpret_cast<float*>(b + C::AUX_OFF);
@@ -236,14 +261,14 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   // Query tiles are visited from the document end downwards: the work-groups
   // resident at the same time hold adjacent key blocks, so they all start at
   // the same tile and stream the same Q / dO tiles through L2 in step.
-  gload(tq_hi);
+  gload_first(tq_hi);
   lstore(0);
   __syncthreads();
   const char* kl = smem + C::K_LDS + (kbw * 32 + lc) * C::KSTR + g * 16;
   const char* vl = smem + C::V_LDS + (kbw * 32 + lc) * C::KSTR + g * 16;
   for (int tq = tq_hi; tq >= tq_lo; --tq) {
     const int st = (tq_hi - tq) & 1;
-    if (tq > tq_lo) gload(tq - 1);
+    if (tq > tq_lo) gload_next();
     const char* b = smem + st * C::STAGE;
     const float* aux_lse = reinterpret_cast<const float*>(b + C::AUX_OFF);
     const float* aux_dl = aux_lse + C::BQ;
@@ -252,7 +277,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     const int64_t tc0 = (int64_t)tq * C::BQ;
     const int first_row = (int)(tc0 >> lgG);
     const int last_row = (int)(min<int64_t>(NG - 1, tc0 + C::BQ - 1) >> lgG);
-    const bool need_mask = first_row < kb_last || doc_start[last_row] > kb0 || tc0 + C::BQ > NG;
+    const bool need_mask = first_row < kb_last || last_row > de0 || tc0 + C::BQ > NG;
 
     f32x16 s, dp;
 #pragma unroll
