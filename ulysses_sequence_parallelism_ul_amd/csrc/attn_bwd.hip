@@ -274,95 +274,95 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   // constant (operand addresses then differ by immediate offsets only)
   auto tile = [&](auto stage, int tq) {
     constexpr int st = decltype(stage)::value;
-      if (tq > tq_lo) gload_next();
-      const char* b = smem + st * C::STAGE;
-      const float* aux_lse = reinterpret_cast<const float*>(b + C::AUX_OFF);
-      const float* aux_dl = aux_lse + C::BQ;
-      const int* aux_row = reinterpret_cast<const int*>(b + C::AUX_OFF) + 2 * C::BQ;
-      const int* aux_ds = aux_row + C::BQ;
-      const int64_t tc0 = (int64_t)tq * C::BQ;
-      const int first_row = (int)(tc0 >> lgG);
-      const int last_row = (int)(min<int64_t>(NG - 1, tc0 + C::BQ - 1) >> lgG);
-      const bool need_mask = first_row < kb_last || last_row > de0 || tc0 + C::BQ > NG;
+    if (tq > tq_lo) gload_next();
+    const char* b = smem + st * C::STAGE;
+    const float* aux_lse = reinterpret_cast<const float*>(b + C::AUX_OFF);
+    const float* aux_dl = aux_lse + C::BQ;
+    const int* aux_row = reinterpret_cast<const int*>(b + C::AUX_OFF) + 2 * C::BQ;
+    const int* aux_ds = aux_row + C::BQ;
+    const int64_t tc0 = (int64_t)tq * C::BQ;
+    const int first_row = (int)(tc0 >> lgG);
+    const int last_row = (int)(min<int64_t>(NG - 1, tc0 + C::BQ - 1) >> lgG);
+    const bool need_mask = first_row < kb_last || last_row > de0 || tc0 + C::BQ > NG;
 
-      f32x16 s, dp;
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) { s[i] = 0.0f; dp[i] = 0.0f; }
-  #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(b + C::Q_OFF + lds_off<D>(qh * 32 + lc, ks * 2 + g));
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(kl + ks * 32);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, s, 0, 0, 0);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(b + C::DO_OFF + lds_off<D>(qh * 32 + lc, ks * 2 + g));
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vl + ks * 32);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, dp, 0, 0, 0);
+    f32x16 s, dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { s[i] = 0.0f; dp[i] = 0.0f; }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(b + C::Q_OFF + lds_off<D>(qh * 32 + lc, ks * 2 + g));
+      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(kl + ks * 32);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, s, 0, 0, 0);
+      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(b + C::DO_OFF + lds_off<D>(qh * 32 + lc, ks * 2 + g));
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vl + ks * 32);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, dp, 0, 0, 0);
+    }
+    // schedule: the operand reads run three MFMAs ahead of the S and dP MFMAs;
+    // the fence keeps the softmax's LDS reads out of this phase (hoisted, they
+    // hold registers the read-ahead needs)
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int j = 0; j < 2 * (D / 16) - 3; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // register i holds query column qh*32 + (i>>3)*16 + g*8 + (i&7) of the tile
+    f32x16 pr, dsr;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int cb = qh * 32 + half * 16 + g * 8;
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(aux_lse + cb);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(aux_lse + cb + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(aux_dl + cb);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(aux_dl + cb + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = half * 8 + e;
+        const float lv = e < 4 ? l0[e] : l1[e - 4];
+        const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -lv));
+        dsr[i] = dp[i] - dv_;
       }
-      // schedule: the operand reads run three MFMAs ahead of the S and dP MFMAs;
-      // the fence keeps the softmax's LDS reads out of this phase (hoisted, they
-      // hold registers the read-ahead needs)
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-  #pragma unroll
-      for (int j = 0; j < 2 * (D / 16) - 3; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    // one uniform branch around the masking of the whole tile (branch-free inside)
+    if (need_mask) {
+      typedef int i32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int cb = qh * 32 + (q4 >> 1) * 16 + g * 8 + (q4 & 1) * 4;
+        const i32x4 rr = *reinterpret_cast<const i32x4*>(aux_row + cb);
+        const i32x4 dd = *reinterpret_cast<const i32x4*>(aux_ds + cb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[q4 * 4 + e] = (key <= rr[e] && key >= dd[e]) ? pr[q4 * 4 + e] : 0.0f;
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      // register i holds query column qh*32 + (i>>3)*16 + g*8 + (i&7) of the tile
-      f32x16 pr, dsr;
-  #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int cb = qh * 32 + half * 16 + g * 8;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(aux_lse + cb);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(aux_lse + cb + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(aux_dl + cb);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(aux_dl + cb + 4);
-  #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = half * 8 + e;
-          const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float dv_ = e < 4 ? d0[e] : d1[e - 4];
-          pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -lv));
-          dsr[i] = dp[i] - dv_;
-        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dsr[i] *= pr[i];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 bp = pack8(pr, kk * 8);
+      const bf16x8 bs = pack8(dsr, kk * 8);
+      const int k0 = qh * 32 + kk * 16;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 adot = lds_tr_a<D>(b + C::DO_OFF, db * 32, k0, l);
+        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adot, bp, dvt[db], 0, 0, 0);
+        const bf16x8 aqt = lds_tr_a<D>(b + C::Q_OFF, db * 32, k0, l);
+        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, bs, dkt[db], 0, 0, 0);
       }
-      // one uniform branch around the masking of the whole tile (branch-free inside)
-      if (need_mask) {
-        typedef int i32x4 __attribute__((ext_vector_type(4)));
-  #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int cb = qh * 32 + (q4 >> 1) * 16 + g * 8 + (q4 & 1) * 4;
-          const i32x4 rr = *reinterpret_cast<const i32x4*>(aux_row + cb);
-          const i32x4 dd = *reinterpret_cast<const i32x4*>(aux_ds + cb);
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) pr[q4 * 4 + e] = (key <= rr[e] && key >= dd[e]) ? pr[q4 * 4 + e] : 0.0f;
-        }
-      }
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) dsr[i] *= pr[i];
-  #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 bp = pack8(pr, kk * 8);
-        const bf16x8 bs = pack8(dsr, kk * 8);
-        const int k0 = qh * 32 + kk * 16;
-  #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 adot = lds_tr_a<D>(b + C::DO_OFF, db * 32, k0, l);
-          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adot, bp, dvt[db], 0, 0, 0);
-          const bf16x8 aqt = lds_tr_a<D>(b + C::Q_OFF, db * 32, k0, l);
-          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, bs, dkt[db], 0, 0, 0);
-        }
-      }
-      // schedule: 4 transpose reads in flight ahead of the dV/dK MFMAs (two per MFMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-  #pragma unroll
-      for (int j = 0; j < D / 8 - 2; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (tq > tq_lo) lstore(st ^ 1);
-      __syncthreads();
+    }
+    // schedule: 4 transpose reads in flight ahead of the dV/dK MFMAs (two per MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int j = 0; j < D / 8 - 2; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (tq > tq_lo) lstore(st ^ 1);
+    __syncthreads();
   };
   for (int tq = tq_hi; tq >= tq_lo; tq -= 2) {
     tile(std::integral_constant<int, 0>(), tq);

@@ -182,94 +182,94 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_bf16_kernel(
   // constant (operand addresses then differ by immediate offsets only)
   auto tile = [&](auto stage, int t) {
     constexpr int st = decltype(stage)::value;
-      if (t < t_hi) gload(t + 1);
-      const char* kb_l = smem + st * C::STAGE;
-      const char* vb_l = kb_l + C::KBYTES;
+    if (t < t_hi) gload(t + 1);
+    const char* kb_l = smem + st * C::STAGE;
+    const char* vb_l = kb_l + C::KBYTES;
 
-      // S^T = K Q^T for 64 keys x 32 columns
-      f32x16 s[2];
-  #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-  #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-  #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_l + (kb * 32 + lc) * C::KSTR + ks * 32 + g * 16);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
-        }
+    // S^T = K Q^T for 64 keys x 32 columns
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_l + (kb * 32 + lc) * C::KSTR + ks * 32 + g * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
       }
-      // schedule: 8 K reads in flight ahead of the 16 MFMAs (the compiler's own
-      // order waits on each read right before its MFMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 LDS reads
-  #pragma unroll
-      for (int j = 0; j < 2 * (D / 16) - 8; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      // the first two 16-key steps of V^T travel during the softmax
-      bf16x8 va[2][D / 32];
-  #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-  #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          va[tt][db] = *reinterpret_cast<const bf16x8*>(vb_l + (db * 32 + lc) * C::VSTR + tt * 32 + g * 16);
+    }
+    // schedule: 8 K reads in flight ahead of the 16 MFMAs (the compiler's own
+    // order waits on each read right before its MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 LDS reads
+#pragma unroll
+    for (int j = 0; j < 2 * (D / 16) - 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    // the first two 16-key steps of V^T travel during the softmax
+    bf16x8 va[2][D / 32];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        va[tt][db] = *reinterpret_cast<const bf16x8*>(vb_l + (db * 32 + lc) * C::VSTR + tt * 32 + g * 16);
 
-      const int t0 = t * C::BN;
-      if (t0 + C::BN - 1 > r_first || t0 < ds_last) {
-  #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kv = t0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-            if (!(kv <= row && kv >= ds_c)) s[kb][i] = -INFINITY;
-          }
-      }
-
-      float mx = s[0][0];
-  #pragma unroll
+    const int t0 = t * C::BN;
+    if (t0 + C::BN - 1 > r_first || t0 < ds_last) {
+#pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-  #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = pair_max(mx);
-      const float mnew = mx * sl2;
-      const bool up = mnew > m_run + kRescaleSlack;
-      if (__any(up)) {
-        const float mset = up ? mnew : m_run;
-        const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mset) : 1.0f;
-        l_run *= alpha;
-  #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-        m_run = mset;
-      }
-      const float ms = m_run == -INFINITY ? 0.0f : m_run;
-      float psum = 0.0f;
-  #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], sl2, -ms));
-          s[kb][i] = p;
-          psum += p;
+          const int kv = t0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+          if (!(kv <= row && kv >= ds_c)) s[kb][i] = -INFINITY;
         }
-      l_run += psum;
+    }
 
-      // O^T += V^T P^T over the 64 keys (4 steps of 16)
-  #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const bf16x8 pb = pack8(s[tt >> 1], (tt & 1) * 8);
-  #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 a =
-              tt < 2 ? va[tt][db] : *reinterpret_cast<const bf16x8*>(vb_l + (db * 32 + lc) * C::VSTR + tt * 32 + g * 16);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
-        }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = pair_max(mx);
+    const float mnew = mx * sl2;
+    const bool up = mnew > m_run + kRescaleSlack;
+    if (__any(up)) {
+      const float mset = up ? mnew : m_run;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mset) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m_run = mset;
+    }
+    const float ms = m_run == -INFINITY ? 0.0f : m_run;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], sl2, -ms));
+        s[kb][i] = p;
+        psum += p;
       }
+    l_run += psum;
 
-      if (t < t_hi) lstore(st ^ 1);
-      __syncthreads();
+    // O^T += V^T P^T over the 64 keys (4 steps of 16)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bf16x8 pb = pack8(s[tt >> 1], (tt & 1) * 8);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 a =
+            tt < 2 ? va[tt][db] : *reinterpret_cast<const bf16x8*>(vb_l + (db * 32 + lc) * C::VSTR + tt * 32 + g * 16);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+      }
+    }
+
+    if (t < t_hi) lstore(st ^ 1);
+    __syncthreads();
   };
   for (int t = t_lo; t <= t_hi; t += 2) {
     tile(std::integral_constant<int, 0>(), t);
