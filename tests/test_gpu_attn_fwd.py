@@ -56,6 +56,10 @@ CASES = [
     (1500, 4, 2, 64, "random"),
     (2048, 16, 1, 128, "random"),
     (3000, 4, 1, 128, "single"),
+    # several KV heads per rank, group sizes 2 and 4, odd head counts
+    (600, 8, 4, 128, "random"),
+    (333, 12, 3, 64, "random"),
+    (1100, 6, 3, 128, "random"),
 ]
 
 
