@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
       float* af = reinterpret_cast<float*>(b + C::AUX_OFF);
       int* ai = reinterpret_cast<int*>(b + C::AUX_OFF);
       af[tid] = a_lse * kLog2e;
-      af[C::BQ + tid] = a_dl;
+      af[C::BQ + tid] = -a_dl;  // stored negated: it seeds the dP accumulator
       ai[2 * C::BQ + tid] = a_row;
       ai[3 * C::BQ + tid] = a_ds;
     }
@@ -285,9 +285,22 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     const int last_row = (int)(min<int64_t>(NG - 1, tc0 + C::BQ - 1) >> lgG);
     const bool need_mask = first_row < kb_last || last_row > de0 || tc0 + C::BQ > NG;
 
+    // register i holds query column qh*32 + (i>>3)*16 + g*8 + (i&7) of the
+    // tile; dP accumulates onto -delta of its column, so the MFMAs give dP - delta
     f32x16 s, dp;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { s[i] = 0.0f; dp[i] = 0.0f; }
+    for (int half = 0; half < 2; ++half) {
+      const int cb = qh * 32 + half * 16 + g * 8;
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(aux_dl + cb);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(aux_dl + cb + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dp[half * 8 + e] = d0[e];
+        dp[half * 8 + 4 + e] = d1[e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const bf16x8 aq = *reinterpret_cast<const bf16x8*>(b + C::Q_OFF + lds_off<D>(qh * 32 + lc, ks * 2 + g));
@@ -297,10 +310,11 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
       const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vl + ks * 32);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, dp, 0, 0, 0);
     }
-    // schedule: the operand reads run three MFMAs ahead of the S and dP MFMAs;
+    // schedule: the operand reads run three MFMAs ahead of the S and dP MFMAs
+    // (the delta seeds are read first);
     // the fence keeps the softmax's LDS reads out of this phase (hoisted, they
     // hold registers the read-ahead needs)
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6 + 4, 0);  // + the 4 delta seed reads
 #pragma unroll
     for (int j = 0; j < 2 * (D / 16) - 3; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -308,22 +322,18 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // register i holds query column qh*32 + (i>>3)*16 + g*8 + (i&7) of the tile
     f32x16 pr, dsr;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int cb = qh * 32 + half * 16 + g * 8;
       const f32x4 l0 = *reinterpret_cast<const f32x4*>(aux_lse + cb);
       const f32x4 l1 = *reinterpret_cast<const f32x4*>(aux_lse + cb + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(aux_dl + cb);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(aux_dl + cb + 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = half * 8 + e;
         const float lv = e < 4 ? l0[e] : l1[e - 4];
-        const float dv_ = e < 4 ? d0[e] : d1[e - 4];
         pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, -lv));
-        dsr[i] = dp[i] - dv_;
+        dsr[i] = dp[i];
       }
     }
     // one uniform branch around the masking of the whole tile (branch-free inside)
