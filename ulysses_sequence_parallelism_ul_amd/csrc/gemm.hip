@@ -131,7 +131,9 @@ gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int6
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    // the last iteration reloads its own tile into the idle stage (harmless),
+    // so the loads and LDS writes stay in one block with the MFMAs
+    gload(min(kt + 1, nk - 1));
     const char* sa = smem + st * kStage;
     const char* sb = sa + kTileBytes;
 #pragma unroll
@@ -148,16 +150,22 @@ gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int6
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+    // the next stage is written into the other buffer (free since the last
+    // barrier) while the MFMAs of this one run
+    lstore(st ^ 1);
     // schedule: the six operand reads of each 16-deep step are issued one step
-    // ahead, under the previous step's eight MFMAs
+    // ahead, under the previous step's eight MFMAs; the next stage's LDS writes
+    // go between the last two groups of eight MFMAs (earlier, they wait on the
+    // global loads)
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
     for (int j = 0; j < kBK / 16 - 2; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    if (kt + 1 < nk) lstore(st ^ 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __syncthreads();
   }
 
