@@ -1,0 +1,109 @@
+"""Host-side logic of bench.py (no GPU): work counts, rocprofv3 summaries,
+the HBM traffic report and its calibration, and the one-GPU refusal."""
+
+import csv
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _pairs_by_loops(pos):
+    doc = oracle.doc_ids(pos)
+    n = len(pos)
+    return sum(1 for i in range(n) for j in range(i + 1) if doc[i] == doc[j])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_useful_pairs_and_document_lengths(seed):
+    pos = synth.random_positions(200, seed)
+    assert bench.useful_pairs(pos) == _pairs_by_loops(pos)
+    lengths = bench.doc_lengths_of(pos)
+    assert lengths.sum() == 200
+    assert len(lengths) == oracle.doc_ids(pos)[-1] + 1
+    # a first token whose position id is not 0 still starts a document
+    pos2 = np.array([3, 4, 0, 1], dtype=np.int32)
+    assert bench.doc_lengths_of(pos2).tolist() == [2, 2]
+    assert bench.useful_pairs(pos2) == 6
+
+
+def test_million_share_counts():
+    pos = synth.workload_positions("million")
+    N = 1 << 20
+    assert bench.useful_pairs(pos) == N * (N + 1) / 2 == 549756338176
+    rd, wr = bench.relayout_bytes_per_step("million")
+    # Q, K, V in and O out (bf16), then dO in and dQ, dK, dV out (fp32), 4 q / 1 KV heads of 128
+    fwd = N * 128 * 2 * (4 + 1 + 1 + 4)
+    bwd = N * 128 * (2 * 4 + 4 * 4 + 4 * 1 + 4 * 1)
+    assert rd == wr == fwd + bwd == 6.5 * 2 ** 30
+    assert bench.relayout_bytes_per_step("llama8b_1doc") == (0, 0)
+
+
+def _write_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0].keys()))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_summarize_rocprof_tables(tmp_path):
+    d = tmp_path / "prof"
+    _write_csv(str(d / "x" / "run_kernel_stats.csv"), [
+        dict(Name="void ul::(anonymous namespace)::dkdv_kernel<128>(...)", Calls=1, TotalDurationNs=2.0e9,
+             AverageNs=2.0e9, MinNs=2.0e9, MaxNs=2.0e9, Percentage=60.0),
+        dict(Name="void at::native::elementwise_kernel<...>", Calls=3, TotalDurationNs=3.0e6, AverageNs=1.0e6,
+             MinNs=1.0e6, MaxNs=1.0e6, Percentage=1.0)])
+    rows = []
+    for c, v in [("SQ_WAVE_CYCLES", 1000.0), ("SQ_WAIT_ANY", 250.0), ("SQ_INSTS_MFMA", 10.0),
+                 ("SQ_INSTS_VALU", 37.0)]:
+        rows.append(dict(Kernel_Name="dkdv_kernel<128>", Counter_Name=c, Counter_Value=v, Start_Timestamp=0,
+                         End_Timestamp=2_000_000))
+    _write_csv(str(d / "x" / "run_counter_collection.csv"), rows)
+    text = bench.summarize_rocprof(str(d))
+    assert "| dkdv_kernel | 1 | 2000.000 | 2000.000 | 2000.000 | 2000.000 | 60.00 |" in text
+    assert "| torch:" in text  # input-generation kernels are listed, marked as torch's
+    assert "| dkdv_kernel | 0.250 |" in text  # SQ_WAIT_ANY / SQ_WAVE_CYCLES
+    assert "| dkdv_kernel | 3.70 |" in text  # SQ_INSTS_VALU / SQ_INSTS_MFMA
+
+
+def test_traffic_report_calibrates_with_the_exchange_copy(tmp_path):
+    rd, wr = bench.relayout_bytes_per_step("million")
+    kib = 1024.0
+
+    def counters(name, relayout_total, dkdv):
+        rows = [dict(Kernel_Name="relayout_kernel", Counter_Name=name, Counter_Value=relayout_total / 8 / kib)
+                for _ in range(8)]
+        rows.append(dict(Kernel_Name="dkdv_kernel<128>", Counter_Name=name, Counter_Value=dkdv / kib))
+        return rows
+
+    fd, wd = tmp_path / "f", tmp_path / "w"
+    # FETCH_SIZE reads twice the bytes a copy moves, WRITE_SIZE exactly them
+    _write_csv(str(fd / "run_counter_collection.csv"), counters("FETCH_SIZE", 2 * rd, 2 * 5.0e12))
+    _write_csv(str(wd / "run_counter_collection.csv"), counters("WRITE_SIZE", wr, 1.0e9))
+    text = bench.traffic_report("million", str(fd), str(wd))
+    assert "FETCH_SIZE x 0.500, WRITE_SIZE x 1.000" in text
+    import json
+    import re
+
+    blob = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+    rec = blob["kernels"]["dkdv_kernel"]
+    assert rec["fetch_bytes"] == pytest.approx(5.0e12)
+    assert rec["write_bytes"] == pytest.approx(1.0e9)
+    assert rec["source_sha256"] == bench._source_sha("dkdv_kernel")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one-GPU" in r.stderr and r.stdout == ""
