@@ -16,8 +16,9 @@
 // Tiling: 256 x 256 output tile per work-group of 8 waves (two per SIMD), each
 // wave 128 rows x 64 columns (4 x 2 blocks of v_mfma_f32_32x32x16_bf16), K in
 // stages of 64 double-buffered in LDS (rows of 128 bytes, 16-byte chunks XOR
-// swizzled by row so 32 rows read at one chunk hit distinct banks), tiles
-// staged through registers one stage ahead.  Work-groups are mapped so each
+// swizzled by row so 32 rows read at one chunk hit distinct banks), the next
+// stage copied global -> LDS by DMA while the current one is multiplied.
+// Work-groups are mapped so each
 // XCD runs groups of 8 row tiles x 4 column tiles together, sharing every K
 // stage's slices of A and B through its L2.
 #include "ul_internal.h"
@@ -31,7 +32,7 @@ constexpr int kRowBytes = kBK * 2;                  // 128 bytes per tile row
 constexpr int kTileBytes = kBM * kRowBytes;         // 32 KiB per operand tile
 constexpr int kStage = 2 * kTileBytes;              // A tile + B tile
 constexpr int kChunksPerTile = kTileBytes / 16;     // 2048
-constexpr int kLoadsPerThread = kChunksPerTile / kThreads;  // 4 per operand
+constexpr int kLoadsPerThread = kChunksPerTile / kThreads;  // 4 per operand (16 bytes each)
 constexpr int kXcds = 8;
 constexpr int kGR = 8, kGC = 4;  // tile group per XCD: 8 row tiles x 4 column tiles
 
@@ -91,31 +92,39 @@ gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int6
   const int n0 = ct * kBN;
   const int wm = w >> 2, wn = w & 3;  // wave grid 2 x 4: 128 rows x 64 columns each
 
-  u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-  auto gload = [&](int kt) {
+  // Tiles go global -> LDS by DMA (global_load_lds_dwordx4): lane l of wave w's
+  // i-th load writes the 16 bytes at LDS block (w * 4 + i) * 1024 + l * 16 of
+  // the tile, so each lane fetches the global chunk that the XOR-swizzled
+  // layout puts there.  Issued as inline assembly so that the compiler does
+  // not order the MFMA phase's LDS reads (of the other stage) behind them; the
+  // wave waits for its own copies before each barrier.
+  const bf16* pa[kLoadsPerThread];
+  const bf16* pb[kLoadsPerThread];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int row = (w * kLoadsPerThread + i) * 8 + (l >> 3);
+    const int chunk = (l & 7) ^ (row & 7);
+    const int64_t am = min<int64_t>(m0 + row, M - 1);   // rows past the end read the last row
+    const int bn = min(n0 + row, Nc - 1);
+    pa[i] = A + am * K + chunk * 8;
+    pb[i] = B + (int64_t)bn * K + chunk * 8;
+  }
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  auto dma = [&](int kt, int st) {
     const int k0 = kt * kBK;
 #pragma unroll
     for (int i = 0; i < kLoadsPerThread; ++i) {
-      const int ch = tid + i * kThreads;
-      const int r = ch >> 3, part = ch & 7;
-      // rows past the end read the last row instead (their results are not stored)
-      const int64_t am = min<int64_t>(m0 + r, M - 1);
-      const int bn = min(n0 + r, Nc - 1);
-      ra[i] = *reinterpret_cast<const u32x4*>(A + am * K + k0 + part * 8);
-      rb[i] = *reinterpret_cast<const u32x4*>(B + (int64_t)bn * K + k0 + part * 8);
+      const uint32_t ba = __builtin_amdgcn_readfirstlane(lds0 + st * kStage + (w * kLoadsPerThread + i) * 1024);
+      const uint32_t bb = ba + kTileBytes;
+      // one wait state between writing M0 and the LDS DMA that reads it
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(ba), "v"(pa[i] + k0)
+                   : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(bb), "v"(pb[i] + k0)
+                   : "memory", "m0");
     }
   };
-  auto lstore = [&](int st) {
-    char* sa = smem + st * kStage;
-    char* sb = sa + kTileBytes;
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      const int ch = tid + i * kThreads;
-      const int r = ch >> 3, part = ch & 7;
-      *reinterpret_cast<u32x4*>(sa + swz(r, part)) = ra[i];
-      *reinterpret_cast<u32x4*>(sb + swz(r, part)) = rb[i];
-    }
-  };
+  auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -126,14 +135,12 @@ gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int6
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = K / kBK;
-  gload(0);
-  lstore(0);
+  dma(0, 0);
+  dma_wait();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    // the last iteration reloads its own tile into the idle stage (harmless),
-    // so the loads and LDS writes stay in one block with the MFMAs
-    gload(min(kt + 1, nk - 1));
+    if (kt + 1 < nk) dma(kt + 1, st ^ 1);  // the other stage is free since the last barrier
     const char* sa = smem + st * kStage;
     const char* sb = sa + kTileBytes;
 #pragma unroll
@@ -150,22 +157,16 @@ gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int6
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    // the next stage is written into the other buffer (free since the last
-    // barrier) while the MFMAs of this one run
-    lstore(st ^ 1);
-    // schedule: the six operand reads of each 16-deep step are issued one step
-    // ahead, under the previous step's eight MFMAs; the next stage's LDS writes
-    // go between the last two groups of eight MFMAs (earlier, they wait on the
-    // global loads)
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    // schedule: nine operand reads ahead, then groups of four MFMAs and three
+    // reads (each 16-deep step needs six reads for eight MFMAs)
+    __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
 #pragma unroll
-    for (int j = 0; j < kBK / 16 - 2; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    for (int j = 0; j < 5; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    dma_wait();
     __syncthreads();
   }
 
