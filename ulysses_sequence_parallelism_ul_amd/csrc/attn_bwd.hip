@@ -193,31 +193,59 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dkt[db][i] = 0.0f; dvt[db][i] = 0.0f; }
 
-  u32x4 rq[C::RPT], rdo[C::RPT];
   float a_lse = 0.0f, a_dl = 0.0f;
   int a_row = -1, a_ds = 0;
-  // A thread loads 16-byte chunk part0 of tile rows r0 + i * RSTEP.  Moving a
-  // tile down by BQ columns (BQ / G whole tokens) moves every source address by
-  // a constant, so only the first tile visited (the one that may run past the
-  // end of the sequence, with clamped columns) computes addresses in full.
-  constexpr int RSTEP = C::kThreads / (D / 8);
-  const int r0 = tid / (D / 8), part0 = tid % (D / 8);
-  const int64_t row_step = (int64_t)RSTEP * Hkv * D, tile_step = (int64_t)C::BQ * Hkv * D;
-  int64_t qoff = col_offset((int64_t)tq_hi * C::BQ + r0, lgG, Hkv, hk, D) + part0 * 8;
+  // Q and dO tiles go global -> LDS by DMA (global_load_lds_dwordx4): lane l
+  // of wave w's i-th copy writes the 16 bytes at byte (w * RPT + i) * 1024 +
+  // l * 16 of the tile, so it fetches the tile row and chunk that the permuted,
+  // swizzled layout keeps there.  Moving a tile down by BQ columns (BQ / G
+  // whole tokens) moves every source address by a constant; only the first
+  // tile visited (the one that may run past the end of the sequence, with
+  // clamped columns) computes its addresses in full.  The copies are inline
+  // assembly so that the compiler does not order this tile's LDS reads behind
+  // them; each wave waits for its own copies before the tile's last barrier.
+  int dr[C::RPT], dch[C::RPT];
+#pragma unroll
+  for (int i = 0; i < C::RPT; ++i) {
+    const int pb = (w * C::RPT + i) * 1024 + l * 16;
+    const int prow = pb / (D * 2), slot = (pb % (D * 2)) >> 4;
+    constexpr int CPR = D / 8;
+    dch[i] = slot ^ ((((prow & 3) << 2) ^ ((prow >> 2) & 3)) & (CPR - 1));
+    dr[i] = tile_row(prow);  // tile_row is an involution
+  }
+  const int64_t tile_step = (int64_t)C::BQ * Hkv * D;
+  int64_t doff[C::RPT];
+#pragma unroll
+  for (int i = 0; i < C::RPT; ++i)
+    doff[i] = col_offset((int64_t)tq_hi * C::BQ + dr[i], lgG, Hkv, hk, D) + dch[i] * 8;
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  auto dma = [&](int st, const int64_t* off) {
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) {
+      const uint32_t mq = __builtin_amdgcn_readfirstlane(lds0 + st * C::STAGE + C::Q_OFF + (w * C::RPT + i) * 1024);
+      const uint32_t md = mq + (C::DO_OFF - C::Q_OFF);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(mq), "v"(q + off[i])
+                   : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(md), "v"(dout + off[i])
+                   : "memory", "m0");
+    }
+  };
+  auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   const int hq_col = (hk << lgG) + (tid & (G - 1));   // query head of aux column tid (tc0 is a multiple of G)
   int arow = (int)(((int64_t)tq_hi * C::BQ + tid) >> lgG);
   int64_t acol = (int64_t)tq_hi * C::BQ + tid;
-  auto gload_first = [&](int tq) {
+  auto gload_first = [&](int tq) {  // into stage 0
     const int64_t tc0 = (int64_t)tq * C::BQ;
+    int64_t off[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) {
       // columns past the end read the last column instead (their P and dS are
-      // masked to zero), so the loads carry no branch
-      const int64_t c = min<int64_t>(tc0 + r0 + i * RSTEP, NG - 1);
-      const int64_t off = col_offset(c, lgG, Hkv, hk, D) + part0 * 8;
-      rq[i] = *reinterpret_cast<const u32x4*>(q + off);
-      rdo[i] = *reinterpret_cast<const u32x4*>(dout + off);
+      // masked to zero), so the copies carry no branch
+      const int64_t c = min<int64_t>(tc0 + dr[i], NG - 1);
+      off[i] = col_offset(c, lgG, Hkv, hk, D) + dch[i] * 8;
     }
+    dma(0, off);
     if (tid < C::BQ) {
       const int64_t c = min<int64_t>(tc0 + tid, NG - 1);
       const int row = (int)(c >> lgG);
@@ -228,15 +256,12 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
       a_ds = doc_start[row];
     }
   };
-  auto gload_next = [&]() {  // the tile below the one loaded last (always inside the sequence)
-    qoff -= tile_step;
+  auto gload_next = [&](int st) {  // the tile below the one loaded last (always inside the sequence)
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) doff[i] -= tile_step;
+    dma(st, doff);
     arow -= C::BQ >> lgG;
     acol -= C::BQ;
-#pragma unroll
-    for (int i = 0; i < C::RPT; ++i) {
-      rq[i] = *reinterpret_cast<const u32x4*>(q + qoff + i * row_step);
-      rdo[i] = *reinterpret_cast<const u32x4*>(dout + qoff + i * row_step);
-    }
     if (tid < C::BQ) {
       a_lse = lse[(int64_t)hq_col * N + arow];
       a_dl = delta[(int64_t)hk * NG + acol];
@@ -244,14 +269,8 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
       a_ds = doc_start[arow];
     }
   };
-  auto lstore = [&](int st) {
+  auto lstore = [&](int st) {  // the aux values of the tile copied last
     char* b = smem + st * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::RPT; ++i) {
-      const int r = r0 + i * RSTEP;
-      *reinterpret_cast<u32x4*>(b + C::Q_OFF + lds_off<D>(tile_row(r), part0)) = rq[i];
-      *reinterpret_cast<u32x4*>(b + C::DO_OFF + lds_off<D>(tile_row(r), part0)) = rdo[i];
-    }
     if (tid < C::BQ) {
       float* af = reinterpret_cast<float*>(b + C::AUX_OFF);
       int* ai = reinterpret_cast<int*>(b + C::AUX_OFF);
@@ -267,6 +286,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   // the same tile and stream the same Q / dO tiles through L2 in step.
   gload_first(tq_hi);
   lstore(0);
+  dma_wait();
   __syncthreads();
   const char* kl = smem + C::K_LDS + (kbw * 32 + lc) * C::KSTR + g * 16;
   const char* vl = smem + C::V_LDS + (kbw * 32 + lc) * C::KSTR + g * 16;
@@ -274,7 +294,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   // constant (operand addresses then differ by immediate offsets only)
   auto tile = [&](auto stage, int tq) {
     constexpr int st = decltype(stage)::value;
-    if (tq > tq_lo) gload_next();
+    if (tq > tq_lo) gload_next(st ^ 1);  // the other stage is free since the last barrier
     const char* b = smem + st * C::STAGE;
     const float* aux_lse = reinterpret_cast<const float*>(b + C::AUX_OFF);
     const float* aux_dl = aux_lse + C::BQ;
@@ -372,6 +392,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     if (tq > tq_lo) lstore(st ^ 1);
+    dma_wait();
     __syncthreads();
   };
   for (int tq = tq_hi; tq >= tq_lo; tq -= 2) {
