@@ -22,7 +22,8 @@
 //    accumulator group covers 8 consecutive columns, 16-byte chunks XOR
 //    swizzled against bank conflicts); the transposed A operands dO^T and Q^T
 //    are read from the same tiles with the gfx950 LDS transpose read
-//    (ds_read_b64_tr_b16), so only 32 KiB per 64-column tile crosses from L2.
+//    (ds_read_b64_tr_b16), so only 32 KiB per 64-column tile crosses from L2;
+//    those tiles are copied global -> LDS by DMA.
 //  * dq_kernel (query-outer, like the forward): a wave owns 32 query columns
 //    with Q and dO in registers; S^T and dP^T are recomputed per key tile and
 //    dQ^T += K^T dS^T takes K^T from the K tile by transpose reads.

@@ -18,9 +18,8 @@
 // stages of 64 double-buffered in LDS (rows of 128 bytes, 16-byte chunks XOR
 // swizzled by row so 32 rows read at one chunk hit distinct banks), the next
 // stage copied global -> LDS by DMA while the current one is multiplied.
-// Work-groups are mapped so each
-// XCD runs groups of 8 row tiles x 4 column tiles together, sharing every K
-// stage's slices of A and B through its L2.
+// Work-groups are mapped so each XCD runs groups of 8 row tiles x 4 column
+// tiles together, sharing every K stage's slices of A and B through its L2.
 #include "ul_internal.h"
 
 namespace ul {
