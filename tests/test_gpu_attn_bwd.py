@@ -145,3 +145,44 @@ def test_full_tensor_reduced_n():
     assert max_abs(np64(dq), ref["dq"]) <= TOL_OUT
     assert max_abs(np64(dk), ref["dk"]) <= TOL_OUT
     assert max_abs(np64(dv), ref["dv"]) <= TOL_OUT
+
+
+def test_peaked_softmax_gradients():
+    """Backward with queries scaled up (nearly one-hot softmax); gradients are
+    held to the bar that grows with their magnitude."""
+    require_gpu()
+    N, Hq, Hkv, D = 700, 4, 1, 128
+    log("bwd peaked softmax")
+    q = synth.to_bf16_torch(synth.normal_f32((N, Hq, D), 41, 1) * 6.0)
+    k = synth.to_bf16_torch(synth.normal_f32((N, Hkv, D), 41, 2))
+    v = synth.to_bf16_torch(synth.normal_f32((N, Hkv, D), 41, 3))
+    do = synth.to_bf16_torch(synth.normal_f32((N, Hq, D), 41, 4))
+    pos = synth.random_positions(N, 41, max_docs=3)
+    dev = [t.to("cuda:0") for t in (q, k, v, do)]
+    pd = _pos_dev(pos)
+    o, lse = ul.attn_fwd(dev[0], dev[1], dev[2], pd)
+    dq, dk, dv = ul.attn_bwd(dev[0], dev[1], dev[2], o, dev[3], lse, pd)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = (t.double().numpy() for t in (q, k, v, do))
+    ref = oracle.attn_bwd(q64, k64, v64, do64, pos)
+    # First-order bound of the kernel's own roundings (unit roundoff u = 2^-8
+    # of bf16): P is rounded for dV^T = dO^T P, dS for dQ = scale dS K and
+    # dK = scale dS^T Q; and delta = rowsum(dO * O) uses the forward's bf16 O,
+    # so the forward's error e_c = sum_d dO (O_gpu - O_exact) shifts every dS of
+    # column c by -P e_c.  With a nearly one-hot softmax these terms are no
+    # longer small next to the 2e-2 bar, so the bar is 2e-2 plus the bound.
+    u, sc = 2.0 ** -8, 1.0 / np.sqrt(D)
+    eo, _ = oracle.attn_fwd(q64, k64, v64, pos)
+    e = np.abs(np.einsum("chd,chd->ch", do64, np64(o) - eo))
+    bq = np.zeros((N, Hq, D)); bk = np.zeros((N, Hkv, D)); bv = np.zeros((N, Hkv, D))
+    for h in range(Hq):
+        P = oracle.attn_probs(q64, k64, pos, head=h)
+        dP = do64[:, h] @ v64[:, 0].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        W = u * np.abs(dS) + P * e[:, h:h + 1]
+        bq[:, h] = sc * (W @ np.abs(k64[:, 0]))
+        bk[:, 0] += sc * (W.T @ np.abs(q64[:, h]))
+        bv[:, 0] += u * (P.T @ np.abs(do64[:, h]))
+    for name, got, bound in (("dq", dq, bq), ("dk", dk, bk), ("dv", dv, bv)):
+        err = np.abs(np64(got) - ref[name])
+        assert np.all(err <= TOL_OUT + 1.5 * bound), (name, float(err.max()), float(bound.max()))
