@@ -132,7 +132,7 @@ struct DkvCfg {
   static constexpr int KVBYTES = BNK * KSTR;
   static constexpr int RSTR = D * 2;       // LDS bytes per Q / dO row (swizzled, unpadded)
   static constexpr int RBYTES = BQ * RSTR;
-  static constexpr int AUX = BQ * 4 * 4;   // lse2, delta, row, doc start per column
+  static constexpr int AUX = BQ * 2 * 4;   // lse2, -delta per column
   // aux first: every operand offset of the second stage then fits a 16-bit
   // LDS immediate
   static constexpr int AUX_OFF = 0, Q_OFF = AUX, DO_OFF = AUX + RBYTES;
@@ -171,6 +171,9 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   const int tq_hi = (int)((((int64_t)(row_end + 1) << lgG) - 1) / C::BQ);
   const int key = kb0 + kbw * 32 + lc;
   const bool kvalid = key < N;
+  // query column c sees this lane's key iff key <= row(c) <= doc_end[key], i.e.
+  // key * G <= c < col_end (past the sequence nothing is visible)
+  const int col_end = (int)min<int64_t>((int64_t)(doc_end[min(key, N - 1)] + 1) << lgG, NG);
 
   // K and V rows of the work-group's keys into LDS (zero past N)
 #pragma unroll
@@ -195,7 +198,6 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     for (int i = 0; i < 16; ++i) { dkt[db][i] = 0.0f; dvt[db][i] = 0.0f; }
 
   float a_lse = 0.0f, a_dl = 0.0f;
-  int a_row = -1, a_ds = 0;
   // Q and dO tiles go global -> LDS by DMA (global_load_lds_dwordx4): lane l
   // of wave w's i-th copy writes the 16 bytes at byte (w * RPT + i) * 1024 +
   // l * 16 of the tile, so it fetches the tile row and chunk that the permuted,
@@ -253,8 +255,6 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
       const int h = (hk << lgG) + (int)(c & (G - 1));
       a_lse = lse[(int64_t)h * N + row];  // scaled by log2(e) when stored, after the load has landed
       a_dl = delta[(int64_t)hk * NG + c];
-      a_row = tc0 + tid < NG ? row : -1;  // -1 masks the column out
-      a_ds = doc_start[row];
     }
   };
   auto gload_next = [&](int st) {  // the tile below the one loaded last (always inside the sequence)
@@ -266,19 +266,14 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     if (tid < C::BQ) {
       a_lse = lse[(int64_t)hq_col * N + arow];
       a_dl = delta[(int64_t)hk * NG + acol];
-      a_row = arow;
-      a_ds = doc_start[arow];
     }
   };
   auto lstore = [&](int st) {  // the aux values of the tile copied last
     char* b = smem + st * C::STAGE;
     if (tid < C::BQ) {
       float* af = reinterpret_cast<float*>(b + C::AUX_OFF);
-      int* ai = reinterpret_cast<int*>(b + C::AUX_OFF);
       af[tid] = a_lse * kLog2e;
       af[C::BQ + tid] = -a_dl;  // stored negated: it seeds the dP accumulator
-      ai[2 * C::BQ + tid] = a_row;
-      ai[3 * C::BQ + tid] = a_ds;
     }
   };
 
@@ -299,8 +294,6 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     const char* b = smem + st * C::STAGE;
     const float* aux_lse = reinterpret_cast<const float*>(b + C::AUX_OFF);
     const float* aux_dl = aux_lse + C::BQ;
-    const int* aux_row = reinterpret_cast<const int*>(b + C::AUX_OFF) + 2 * C::BQ;
-    const int* aux_ds = aux_row + C::BQ;
     const int64_t tc0 = (int64_t)tq * C::BQ;
     const int first_row = (int)(tc0 >> lgG);
     const int last_row = (int)(min<int64_t>(NG - 1, tc0 + C::BQ - 1) >> lgG);
@@ -359,14 +352,21 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     }
     // one uniform branch around the masking of the whole tile (branch-free inside)
     if (need_mask) {
-      typedef int i32x4 __attribute__((ext_vector_type(4)));
+      // register i holds tile column cbase + (i>>3)*16 + (i&7); visible iff that
+      // offset lies in [lo, lo + span]
+      const int cbase = qh * 32 + g * 8;
+      const int c0 = (int)tc0 + cbase;
+      int lo = min(key, N) * G - c0;  // keys past the end: lo > hi below
+      const int hi = col_end - 1 - c0;
+      unsigned span = (unsigned)(hi - lo);
+      if (hi < lo) {
+        lo = 1 << 30;
+        span = 0u;
+      }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int cb = qh * 32 + (q4 >> 1) * 16 + g * 8 + (q4 & 1) * 4;
-        const i32x4 rr = *reinterpret_cast<const i32x4*>(aux_row + cb);
-        const i32x4 dd = *reinterpret_cast<const i32x4*>(aux_ds + cb);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pr[q4 * 4 + e] = (key <= rr[e] && key >= dd[e]) ? pr[q4 * 4 + e] : 0.0f;
+      for (int i = 0; i < 16; ++i) {
+        const int off = (i >> 3) * 16 + (i & 7);
+        pr[i] = (unsigned)(off - lo) <= span ? pr[i] : 0.0f;
       }
     }
 #pragma unroll

@@ -217,13 +217,21 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_bf16_kernel(
 
     const int t0 = t * C::BN;
     if (t0 + C::BN - 1 > r_first || t0 < ds_last) {
+      // register i of block kb holds key t0 + kb*32 + (i>>3)*16 + g*8 + (i&7);
+      // visible iff it lies in [ds_c, row] (empty for a column past the end)
+      const int kbase = t0 + g * 8;
+      int lo = ds_c - kbase;
+      const int hi = row - kbase;
+      unsigned span = (unsigned)(hi - lo);
+      if (hi < lo) {
+        lo = 1 << 30;
+        span = 0u;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kv = t0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-          if (!(kv <= row && kv >= ds_c)) s[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if ((unsigned)(kb * 32 + (i >> 3) * 16 + (i & 7) - lo) > span) s[kb][i] = -INFINITY;
     }
 
     float mx = s[0][0];
