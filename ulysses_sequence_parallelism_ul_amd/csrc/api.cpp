@@ -189,6 +189,12 @@ WsLayout ws_layout(int64_t N, int Hq, int Hkv, int D, ul_dtype dt, bool for_bwd)
   if (for_bwd) {
     L.delta = off; off = align_up(off + (size_t)Hq * N * 4, A);
   }
+  if (dt == UL_BF16) {
+    L.order_col = off; off = align_up(off + (size_t)col_blocks(N, Hq / Hkv) * 4, A);
+    if (for_bwd) {
+      L.order_key = off; off = align_up(off + (size_t)key_blocks(N) * 4, A);
+    }
+  }
   L.total = off;
   return L;
 }
@@ -277,7 +283,8 @@ ul_status ul_attn_fwd(const void* q, const void* k, const void* v, const int32_t
   if (dt == UL_BF16)
     err = ul::launch_attn_fwd_bf16(static_cast<const ul::bf16*>(q), static_cast<const ul::bf16*>(k),
                                    static_cast<const ul::bf16*>(v), ds, static_cast<ul::bf16*>(o), lse,
-                                   reinterpret_cast<ul::bf16*>(w + L.vt), (int)N, Hq, Hkv, D, scale, s);
+                                   reinterpret_cast<ul::bf16*>(w + L.vt), reinterpret_cast<int32_t*>(w + L.order_col),
+                                   (int)N, Hq, Hkv, D, scale, s);
   else
     err = ul::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                   static_cast<const float*>(v), ds, static_cast<float*>(o), lse, (int)N, Hq, Hkv, D,
@@ -318,7 +325,8 @@ ul_status ul_attn_bwd(const void* q, const void* k, const void* v, const void* o
     err = ul::launch_attn_bwd_bf16(
         static_cast<const ul::bf16*>(q), static_cast<const ul::bf16*>(k), static_cast<const ul::bf16*>(v),
         static_cast<const ul::bf16*>(o), static_cast<const ul::bf16*>(dout), lse, ds, de, dq, dk, dv, delta,
-        (int)N, Hq, Hkv, D, scale, s);
+        reinterpret_cast<int32_t*>(w + L.order_col), reinterpret_cast<int32_t*>(w + L.order_key), (int)N, Hq, Hkv, D,
+        scale, s);
   else
     err = ul::launch_attn_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                   static_cast<const float*>(v), static_cast<const float*>(o),
@@ -381,7 +389,9 @@ ul_status ul_rank_attn_fwd(const void* q_seq, const void* k_seq, const void* v_s
                                        reinterpret_cast<const ul::bf16*>(w + W.kh),
                                        reinterpret_cast<const ul::bf16*>(w + W.vh), ds,
                                        reinterpret_cast<ul::bf16*>(w + W.oh), lse_c,
-                                       reinterpret_cast<ul::bf16*>(w + W.att.vt), (int)N, r.qc, r.kc, D, scale, s);
+                                       reinterpret_cast<ul::bf16*>(w + W.att.vt),
+                                       reinterpret_cast<int32_t*>(w + W.att.order_col), (int)N, r.qc, r.kc, D, scale,
+                                       s);
       else
         err = ul::launch_attn_fwd_f32(reinterpret_cast<const float*>(w + W.qh),
                                       reinterpret_cast<const float*>(w + W.kh),
@@ -450,8 +460,9 @@ ul_status ul_rank_attn_bwd(const void* q_seq, const void* k_seq, const void* v_s
         err = ul::launch_attn_bwd_bf16(
             reinterpret_cast<const ul::bf16*>(w + W.qh), reinterpret_cast<const ul::bf16*>(w + W.kh),
             reinterpret_cast<const ul::bf16*>(w + W.vh), reinterpret_cast<const ul::bf16*>(w + W.oh),
-            reinterpret_cast<const ul::bf16*>(w + W.doh), lse_c, ds, de, dqh, dk_out, dv_out, delta, (int)N, r.qc,
-            r.kc, D, scale, s);
+            reinterpret_cast<const ul::bf16*>(w + W.doh), lse_c, ds, de, dqh, dk_out, dv_out, delta,
+            reinterpret_cast<int32_t*>(w + W.att.order_col), reinterpret_cast<int32_t*>(w + W.att.order_key), (int)N,
+            r.qc, r.kc, D, scale, s);
       else
         err = ul::launch_attn_bwd_f32(
             reinterpret_cast<const float*>(w + W.qh), reinterpret_cast<const float*>(w + W.kh),

@@ -88,14 +88,14 @@ __device__ __forceinline__ float pair_sum(float x) {
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ vt,
-    const int32_t* __restrict__ doc_start, bf16* __restrict__ o, float* __restrict__ lse, int N, int Hkv,
-    int lgG, float sl2, int ncb, int nb) {
+    const int32_t* __restrict__ doc_start, const int32_t* __restrict__ order, bf16* __restrict__ o,
+    float* __restrict__ lse, int N, int Hkv, int lgG, float sl2, int nb) {
   using C = FwdCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
   const int G = 1 << lgG;
   const int hk = blockIdx.x % Hkv;
-  const int cb = ncb - 1 - (int)(blockIdx.x / Hkv);  // heaviest column blocks first
+  const int cb = order[blockIdx.x / Hkv];  // heaviest column blocks first
   const int64_t NG = (int64_t)N << lgG;
   const int64_t c0 = (int64_t)cb * C::BMC;
   const int r_first = (int)(c0 >> lgG);
@@ -348,7 +348,7 @@ int ilog2_pow2(int x) {
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* doc_start, bf16* o,
-                                float* lse, bf16* vt_ws, int N, int Hq, int Hkv, int D, float scale,
+                                float* lse, bf16* vt_ws, int32_t* order_ws, int N, int Hq, int Hkv, int D, float scale,
                                 hipStream_t s) {
   hipError_t e = launch_transpose_blocked(v, vt_ws, N, Hkv, Hkv, 0, D, s);
   if (e != hipSuccess) return e;
@@ -356,16 +356,21 @@ hipError_t launch_attn_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, con
   const int nb = (N + kTB - 1) / kTB;
   const float sl2 = scale * kLog2e;
   constexpr int NW = 8;
-  const int64_t ncols = (int64_t)N * (Hq / Hkv);
-  const int ncb = (int)((ncols + NW * 32 - 1) / (NW * 32));
+  static_assert(FwdCfg<128, NW>::BMC == kColBlock && FwdCfg<128, NW>::BN == kKeyTile, "unit sizes of the order");
+  static_assert(FwdCfg<64, NW>::BMC == kColBlock && FwdCfg<64, NW>::BN == kKeyTile, "unit sizes of the order");
+  const int ncb = (int)col_blocks(N, Hq / Hkv);
+  OrderJobs jobs{};
+  jobs.j[0] = OrderJob{order_ws, doc_start, 0, ncb, kColBlock, kKeyTile};
+  e = launch_order(jobs, 1, N, lgG, s);
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((int64_t)ncb * Hkv)), block(NW * 64);
   TimedLaunch timer("attn_fwd_bf16", s);
   if (D == 128)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, NW>), grid, block, 0, s, q, k, vt_ws, doc_start, o, lse, N, Hkv,
-                       lgG, sl2, ncb, nb);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, NW>), grid, block, 0, s, q, k, vt_ws, doc_start, order_ws, o, lse,
+                       N, Hkv, lgG, sl2, nb);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, NW>), grid, block, 0, s, q, k, vt_ws, doc_start, o, lse, N, Hkv,
-                       lgG, sl2, ncb, nb);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, NW>), grid, block, 0, s, q, k, vt_ws, doc_start, order_ws, o, lse,
+                       N, Hkv, lgG, sl2, nb);
   return hipGetLastError();
 }
 

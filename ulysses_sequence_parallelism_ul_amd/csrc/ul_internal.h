@@ -32,6 +32,8 @@ struct WsLayout {
   size_t doc_start = 0, doc_end = 0, scan = 0;  // int32 [N], int32 [N], int32 [2 * nblk]
   size_t vt = 0;     // bf16 fwd: V^T blocked [Hkv][NB][D][kTB]
   size_t delta = 0;  // bwd: float [Hkv][N*G] (query-column order)
+  size_t order_col = 0;  // bf16: int32 launch order of the query-column blocks (forward, dQ)
+  size_t order_key = 0;  // bf16 bwd: int32 launch order of the key blocks (dK/dV)
   size_t total = 0;
 };
 
@@ -53,7 +55,26 @@ struct TimedLaunch {
   }
 };
 
+// Work-group units of the bf16 attention kernels: query-column blocks of
+// kColBlock columns against key tiles of kKeyTile keys (forward, dQ), and key
+// blocks of kKeyBlock keys against query-column tiles of kColTile columns (dK/dV).
+constexpr int kColBlock = 256, kKeyTile = 64, kKeyBlock = 128, kColTile = 64;
+inline int64_t col_blocks(int64_t N, int G) { return (N * G + kColBlock - 1) / kColBlock; }
+inline int64_t key_blocks(int64_t N) { return (N + kKeyBlock - 1) / kKeyBlock; }
+
+// One launch order to compute: units 0 .. units-1 sorted by decreasing work.
+struct OrderJob {
+  int32_t* order;        // out: int32 [units], a permutation of 0 .. units-1
+  const int32_t* bound;  // doc_end (key blocks) or doc_start (column blocks), int32 [N]
+  int key_blocks;        // 1: key blocks of `unit` keys over column tiles of `tile`; 0: the transpose
+  int units, unit, tile;
+};
+struct OrderJobs {
+  OrderJob j[2];
+};
+
 // ---- launchers (enqueue only; arguments already validated) ----
+hipError_t launch_order(const OrderJobs& jobs, int njobs, int N, int lgG, hipStream_t s);
 hipError_t launch_relayout(const void* src, void* dst, int64_t N, int H, int D, int P, int rank,
                            int elem_bytes, bool seq_to_head, hipStream_t s);
 hipError_t launch_doc_bounds(const int32_t* pos, int32_t* doc_start, int32_t* doc_end,
@@ -85,15 +106,16 @@ int ce_max_resident_vocab(int elem_bytes);
 // dst[i] += src[i] for n floats (n a multiple of 4, 16-byte aligned buffers).
 hipError_t launch_add_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 hipError_t launch_attn_fwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* doc_start,
-                                bf16* o, float* lse, bf16* vt_ws, int N, int Hq, int Hkv, int D,
-                                float scale, hipStream_t s);
+                                bf16* o, float* lse, bf16* vt_ws, int32_t* order_ws, int N, int Hq, int Hkv,
+                                int D, float scale, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const int32_t* doc_start,
                                float* o, float* lse, int N, int Hq, int Hkv, int D, float scale,
                                hipStream_t s);
 hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
                                 const bf16* dout, const float* lse, const int32_t* doc_start,
                                 const int32_t* doc_end, float* dq, float* dk, float* dv, float* delta,
-                                int N, int Hq, int Hkv, int D, float scale, hipStream_t s);
+                                int32_t* order_col, int32_t* order_key, int N, int Hq, int Hkv, int D, float scale,
+                                hipStream_t s);
 hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                                const float* dout, const float* lse, const int32_t* doc_start,
                                const int32_t* doc_end, float* dq, float* dk, float* dv, float* delta,
