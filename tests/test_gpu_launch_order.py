@@ -4,8 +4,8 @@ The order does not change any output (each work-group writes only its own
 rows); these tests check the order itself.  The attention workspace ends with
 the order of the query-column blocks (forward, dQ) and, for the backward, the
 order of the key blocks (dK/dV), each int32 and padded to 256 bytes.  A unit's
-work is the number of tiles its loop visits; units are bucketed into 4096
-equal-width work buckets (width (max work + 1) / 4096), heaviest bucket first,
+work is the number of tiles its loop visits; units are bucketed into 2048
+equal-width work buckets (width (max work + 1) / 2048), heaviest bucket first,
 and within a bucket kept in the order in which work grows inside a document:
 key blocks ascending, column blocks descending.
 """
@@ -20,7 +20,7 @@ from gpu_helpers import log, require_gpu
 
 pytestmark = pytest.mark.gpu
 
-COL_BLOCK, KEY_TILE, KEY_BLOCK, COL_TILE, BUCKETS = 256, 64, 128, 64, 4096
+COL_BLOCK, KEY_TILE, KEY_BLOCK, COL_TILE, BUCKETS = 256, 64, 128, 64, 2048
 
 
 def _pad(n):
@@ -54,7 +54,7 @@ def _col_work(doc_start, N, G):
     return rl // KEY_TILE - doc_start[rf] // KEY_TILE + 1
 
 
-@pytest.mark.parametrize("case", ["one_document", "train_packed", "random", "lone_tokens"])
+@pytest.mark.parametrize("case", ["one_document", "train_packed", "random", "lone_tokens", "small", "one_token"])
 def test_orders_are_heaviest_first_permutations(case):
     require_gpu()
     Hq, Hkv, D = 4, 1, 128
@@ -65,6 +65,10 @@ def test_orders_are_heaviest_first_permutations(case):
         pos = synth.random_positions(50_000, 5, max_docs=40)
     elif case == "lone_tokens":
         pos = np.zeros(3000, dtype=np.int32)
+    elif case == "small":  # fewer units than waves in the order kernel
+        pos = synth.random_positions(1000, 3, max_docs=4)
+    elif case == "one_token":
+        pos = np.zeros(1, dtype=np.int32)
     else:
         pos = np.arange(70_000, dtype=np.int32)
     N = len(pos)

@@ -9,10 +9,11 @@
 // classic longest-processing-time list schedule; this kernel computes that
 // order from the document bounds on the device, so the host never waits.
 //
-// One work-group per order: the work of every unit, its maximum, a histogram
-// over kBuckets equal-width work buckets, the suffix sums of the histogram
-// (heaviest bucket first), then a stable scatter of unit indices, so the order
-// is deterministic.  Each unit writes only its own outputs: results do not
+// One work-group per order: the work of every unit, its maximum, histograms
+// over kBuckets equal-width work buckets (one per wave, each over its own
+// contiguous segment of units), the suffix sums of the totals (heaviest bucket
+// first) and each wave's first place per bucket, then a stable scatter by all
+// waves at once, so the order is deterministic.  Each unit writes only its own outputs: results do not
 // depend on the order.
 #include "ul_internal.h"
 
@@ -20,9 +21,10 @@ namespace ul {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kBuckets = 4096;
+constexpr int kWaves = kThreads / 64;
+constexpr int kBuckets = 2048;
 constexpr int kPer = kBuckets / kThreads;
-constexpr int kBatch = 8;
+constexpr int kBatch = 4;
 
 __device__ inline int unit_work(const OrderJob& J, int N, int lgG, int u) {
   if (J.key_blocks) {
@@ -49,28 +51,38 @@ __device__ inline int bucket_of(int w, int wmax) {
 
 __global__ void __launch_bounds__(kThreads) order_kernel(OrderJobs jobs, int N, int lgG) {
   const OrderJob J = jobs.j[blockIdx.x];
-  __shared__ int cnt[kBuckets];
-  __shared__ int wsum[kThreads / 64];
+  // hist[w][b]: units of bucket b in wave w's segment of the visit order, then
+  // the place where the next of them goes
+  __shared__ int hist[kWaves][kBuckets];
+  __shared__ int wsum[kWaves];
   __shared__ int wmax_s;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int b = tid; b < kBuckets; b += kThreads) cnt[b] = 0;
+  for (int x = tid; x < kWaves * kBuckets; x += kThreads) (&hist[0][0])[x] = 0;
   if (tid == 0) wmax_s = 0;
   __syncthreads();
+
+  // visit order: key blocks ascending, column blocks descending (the order in
+  // which work grows inside a document); wave w owns visits [v0, v1)
+  auto unit_at = [&](int i) { return J.key_blocks ? i : J.units - 1 - i; };
+  const int seg = (J.units + kWaves - 1) / kWaves;
+  const int v0 = min(J.units, wv * seg), v1 = min(J.units, v0 + seg);
 
   int m = 0;
   for (int u = tid; u < J.units; u += kThreads) m = max(m, unit_work(J, N, lgG, u));
   atomicMax(&wmax_s, m);
   __syncthreads();
   const int wmax = wmax_s;
-  for (int u = tid; u < J.units; u += kThreads) atomicAdd(&cnt[bucket_of(unit_work(J, N, lgG, u), wmax)], 1);
+  for (int i = v0 + lane; i < v1; i += 64) atomicAdd(&hist[wv][bucket_of(unit_work(J, N, lgG, unit_at(i)), wmax)], 1);
   __syncthreads();
 
-  // exclusive sums from the heaviest bucket down: thread t owns the kPer
-  // buckets kBuckets-1-(t*kPer) ... kBuckets-1-(t*kPer+kPer-1)
+  // bucket totals, exclusive sums from the heaviest bucket down (thread t owns
+  // buckets kBuckets-1-(t*kPer+i)), then each wave's first place per bucket
   int c[kPer], s = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    c[i] = cnt[kBuckets - 1 - (tid * kPer + i)];
+    const int b = kBuckets - 1 - (tid * kPer + i);
+    c[i] = 0;
+    for (int w = 0; w < kWaves; ++w) c[i] += hist[w][b];
     s += c[i];
   }
   int incl = s;  // inclusive scan over the wave
@@ -80,37 +92,36 @@ __global__ void __launch_bounds__(kThreads) order_kernel(OrderJobs jobs, int N, 
   }
   if (lane == 63) wsum[wv] = incl;
   __syncthreads();
-  int before = 0;
-  for (int i = 0; i < wv; ++i) before += wsum[i];
-  int base = before + incl - s;
+  int base = incl - s;
+  for (int i = 0; i < wv; ++i) base += wsum[i];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    cnt[kBuckets - 1 - (tid * kPer + i)] = base;
+    const int b = kBuckets - 1 - (tid * kPer + i);
+    int at = base;
+    for (int w = 0; w < kWaves; ++w) {
+      const int n = hist[w][b];
+      hist[w][b] = at;
+      at += n;
+    }
     base += c[i];
   }
   __syncthreads();
 
-  // stable scatter by one wave, 64 units per step: a lane's place is its
-  // bucket's next free place plus the number of lower lanes in the same
-  // bucket.  Units are visited in the order in which work grows within a
-  // document (key blocks ascending, column blocks descending), so one document
-  // keeps its units in their natural order.  The buckets of kBatch steps are
+  // stable scatter, each wave over its own segment, 64 visits per step: a
+  // lane's place is its bucket's next place in this wave's row plus the number
+  // of lower lanes in the same bucket.  The buckets of kBatch steps are
   // computed together so their loads overlap.
-  if (wv != 0) return;
   const uint64_t below = (1ull << lane) - 1;
-  for (int i0 = 0; i0 < J.units; i0 += 64 * kBatch) {
+  for (int i0 = v0; i0 < v1; i0 += 64 * kBatch) {
     int bb[kBatch];
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
       const int i = i0 + r * 64 + lane;
-      const int u = J.key_blocks ? i : J.units - 1 - i;
-      bb[r] = i < J.units ? bucket_of(unit_work(J, N, lgG, u), wmax) : -1;
+      bb[r] = i < v1 ? bucket_of(unit_work(J, N, lgG, unit_at(i)), wmax) : -1;
     }
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
       const int b = bb[r];
-      const int i = i0 + r * 64 + lane;
-      const int u = J.key_blocks ? i : J.units - 1 - i;
       int rank = 0, group = 0;
       uint64_t rem = __ballot(b >= 0);
       while (rem) {
@@ -123,9 +134,9 @@ __global__ void __launch_bounds__(kThreads) order_kernel(OrderJobs jobs, int N, 
         rem &= ~m;
       }
       if (b >= 0) {
-        const int at = cnt[b];
-        J.order[at + rank] = u;
-        if (rank == group - 1) cnt[b] = at + group;  // the group's last lane advances its bucket
+        const int at = hist[wv][b];
+        J.order[at + rank] = unit_at(i0 + r * 64 + lane);
+        if (rank == group - 1) hist[wv][b] = at + group;  // the group's last lane advances its bucket
       }
     }
   }
