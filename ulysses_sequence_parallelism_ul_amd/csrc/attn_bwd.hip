@@ -127,8 +127,7 @@ __global__ void __launch_bounds__(256) delta_bf16_kernel(const bf16* __restrict_
 // fetched in: with its loop starting 44 bytes into a line dQ ran 3 % slower
 // than at 0, 24 or 32 bytes (same box, N = 1M, identical loop code).  The
 // counts hold for the code as it stands; any change to a prologue moves its
-// loop, so the offset is to be re-read from the disassembly (the target of the
-// loop's backward branch) after such a change.
+// loop (tests/test_code_layout.py disassembles the build and checks both).
 #define UL_CODE_PAD(n) asm volatile(".rept " #n "\ns_nop 0\n.endr")
 
 template <int D>
