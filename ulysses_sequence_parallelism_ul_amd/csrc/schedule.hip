@@ -13,8 +13,8 @@
 // over kBuckets equal-width work buckets (one per wave, each over its own
 // contiguous segment of units), the suffix sums of the totals (heaviest bucket
 // first) and each wave's first place per bucket, then a stable scatter by all
-// waves at once, so the order is deterministic.  Each unit writes only its own outputs: results do not
-// depend on the order.
+// waves at once, so the order is deterministic.  Each unit writes only its own
+// outputs: results do not depend on the order.
 #include "ul_internal.h"
 
 namespace ul {
