@@ -2,6 +2,7 @@
 the HBM traffic report and its calibration, and the one-GPU refusal."""
 
 import csv
+import json
 import os
 import subprocess
 import sys
@@ -107,3 +108,48 @@ def test_more_than_one_gpu_is_refused():
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one-GPU" in r.stderr and r.stdout == ""
+
+
+def _smi_metric_json(power, clocks):
+    clock = {f"gfx_{i}": {"clk": {"value": c, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
+                          "max_clk": {"value": 2400, "unit": "MHz"}, "clk_locked": "DISABLED"}
+             for i, c in enumerate(clocks)}
+    clock["mem_0"] = {"clk": {"value": 2000, "unit": "MHz"}}
+    clock["vclk_0"] = "N/A"
+    return json.dumps({"gpu_data": [{"gpu": 0, "power": {"socket_power": {"value": power, "unit": "W"},
+                                                         "gfx_voltage": "N/A"}, "clock": clock}]})
+
+
+def test_power_clock_parsing():
+    """Board power and the mean graphics clock over the XCDs from amd-smi's JSON; memory clocks are ignored."""
+    p, c = bench.parse_smi_metric(_smi_metric_json(1309, [1834, 1763, 1833, 1720, 1873, 1776, 1882, 1798]))
+    assert p == 1309.0 and c == pytest.approx(1809.875)
+    p, c = bench.parse_smi_metric(_smi_metric_json("N/A", []))
+    assert p is None and c is None
+    listing = json.dumps([{"gpu": 0, "bdf": "0000:05:00.0"}, {"gpu": 3, "bdf": "0000:F5:00.0"}])
+    assert bench.smi_index_of("0000:f5:00", listing) == 3
+    assert bench.smi_index_of("0000:75:00", listing) is None
+
+
+def test_power_sampler_without_a_device_reports_nothing():
+    """No PCI address (no GPU here): no polling thread, every summary field None, zero samples."""
+    class _NoCuda:
+        class cuda:
+            @staticmethod
+            def get_device_properties(i):
+                raise RuntimeError("no GPU")
+
+    s = bench.PowerSampler(_NoCuda)
+    with s:
+        pass
+    out = s.summary()
+    assert out["samples"] == 0 and out["board_power_w"] is None and out["gfx_clock_mhz"] is None
+
+
+def test_power_clock_context_scales_the_peak_by_the_clock():
+    roof = {"bound": "mfma", "achieved": 1100.0}
+    out = bench.power_clock_context({"samples": 3, "gfx_clock_mhz": 1800.0, "board_power_w": 1330.0}, roof)
+    assert out["mfma_peak_at_clock_tflops"] == pytest.approx(1875.0)
+    assert out["dominant_frac_at_clock"] == pytest.approx(1100.0 / 1875.0)
+    out = bench.power_clock_context({"samples": 0, "gfx_clock_mhz": None, "board_power_w": None}, roof)
+    assert "mfma_peak_at_clock_tflops" not in out
