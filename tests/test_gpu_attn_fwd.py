@@ -116,6 +116,34 @@ def test_workload_sampled_rows(name):
     assert max_abs(np64(lse[:, torch.from_numpy(r).to("cuda:0")]), el) <= TOL_LSE
 
 
+@pytest.mark.timeout(600)
+def test_packed_workload_full_tensor_per_document():
+    """The packed 131,072-token workload (4 q / 1 KV heads, D=128, bf16, 23 documents) on whole tensors:
+    every document's O and LSE against the explicit-mask oracle run on that document alone (a packed
+    sequence equals its documents run separately, a property the oracle tests pin)."""
+    require_gpu()
+    w = synth.WORKLOADS["llama8b_packed"]
+    N = w["N"]
+    Hq, Hkv = w["Hq"] // w["P"], w["Hkv"] // w["P"]
+    d, host = dev_inputs(N, Hq, Hkv, w["D"], w["index"], torch.bfloat16)
+    pos = synth.workload_positions("llama8b_packed")
+    o, lse = ul.attn_fwd(d["q"], d["k"], d["v"], _pos_dev(pos))
+    torch.cuda.synchronize()
+    o64, lse64 = np64(o), np64(lse)
+    q64, k64, v64 = (host[x].double().numpy() for x in ("q", "k", "v"))
+    starts = np.flatnonzero(pos == 0)
+    ends = np.r_[starts[1:], N]
+    assert ends[-1] == N and starts[0] == 0
+    worst_o = worst_l = 0.0
+    for s, e in zip(starts, ends):
+        eo, el = oracle.attn_fwd(q64[s:e], k64[s:e], v64[s:e], None)
+        worst_o = max(worst_o, max_abs(o64[s:e], eo))
+        worst_l = max(worst_l, max_abs(lse64[:, s:e], el))
+        log(f"fwd llama8b_packed document [{s}, {e}): max|dO| so far {worst_o:.3e}, max|dLSE| {worst_l:.3e}")
+    assert worst_o <= TOL_OUT
+    assert worst_l <= TOL_LSE
+
+
 def test_full_tensor_llama_share_reduced_n():
     """Same recipe as the packed workload at N=8192, whole tensors against the full oracle."""
     require_gpu()

@@ -6,7 +6,8 @@ Checks: exchanges bit-exact on full tensors against a torch slice (an
 independent library routine) and on sampled rows against the oracle; forward
 and dQ on sampled rows against the oracle; dK/dV on the last keys of
 documents against the oracle; per-document dK/dV sums; the Q = 0 closed forms
-at N = 1M; determinism.
+at N = 1M; determinism; and, for the training share, every document's O, LSE,
+dQ, dK and dV on whole tensors against the oracle run per document.
 """
 
 import numpy as np
@@ -110,6 +111,33 @@ def test_full_path(name):
         L = e - s
         assert np.abs(dk64[s:e].sum(axis=0)).max() <= TOL_OUT * np.sqrt(L)
         assert np.abs(dv64[s:e].sum(axis=0) - np64(do_sum[s:e].sum(dim=0))).max() <= TOL_OUT * np.sqrt(L)
+
+
+@pytest.mark.timeout(900)
+def test_training_share_full_tensor_per_document():
+    """The packed training share (N=262144, 39 documents, 4 q / 1 KV heads, D=128, bf16) on whole
+    tensors: O, LSE, dQ, dK and dV of every document against the explicit-mask oracle run on that
+    document alone (a packed sequence equals its documents run separately, pinned by the oracle tests)."""
+    require_gpu()
+    log("path train_packed: full tensors per document")
+    r = _run("train_packed")
+    N, pos = r["N"], r["pos"]
+    q64, k64, v64, do64 = (np64(r[x]) for x in ("q", "k", "v", "do"))
+    gpu = {x: np64(r[x]) for x in ("o", "dq", "dk", "dv")}
+    lse64 = np64(r["lse"])
+    starts = np.flatnonzero(pos == 0)
+    ends = np.r_[starts[1:], N]
+    assert starts[0] == 0 and len(starts) == len(np.unique(oracle.doc_bounds(pos)[0]))
+    worst = dict.fromkeys(("o", "lse", "dq", "dk", "dv"), 0.0)
+    for s, e in zip(starts, ends):
+        ref = oracle.attn_bwd(q64[s:e], k64[s:e], v64[s:e], do64[s:e], None)
+        for x in ("o", "dq", "dk", "dv"):
+            worst[x] = max(worst[x], max_abs(gpu[x][s:e], ref[x]))
+        worst["lse"] = max(worst["lse"], max_abs(lse64[:, s:e], ref["lse"]))
+        log(f"path train_packed document [{s}, {e}): worst so far " + ", ".join(f"{x} {v:.3e}" for x, v in worst.items()))
+    for x in ("o", "dq", "dk", "dv"):
+        assert worst[x] <= TOL_OUT, (x, worst[x])
+    assert worst["lse"] <= TOL_LSE
 
 
 @pytest.mark.timeout(300)
