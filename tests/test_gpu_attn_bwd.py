@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 import ulysses_sequence_parallelism_ul_amd as ul
-from gpu_helpers import TOL_OUT, dev_inputs, grad_bar, log, max_abs, np64, require_gpu
+from gpu_helpers import TOL_LSE, TOL_OUT, dev_inputs, grad_bar, log, max_abs, np64, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -145,6 +145,28 @@ def test_full_tensor_reduced_n():
     assert max_abs(np64(dq), ref["dq"]) <= TOL_OUT
     assert max_abs(np64(dk), ref["dk"]) <= TOL_OUT
     assert max_abs(np64(dv), ref["dv"]) <= TOL_OUT
+
+
+@pytest.mark.timeout(600)
+def test_one_document_32k_full_tensor():
+    """The one-document Llama-8B rank share (N=32768, 4 q / 1 KV heads, D=128, bf16) on whole tensors:
+    O, LSE, dQ, dK and dV against the explicit-mask oracle (the million-token share's kernels and launch
+    configuration at a size the oracle finishes)."""
+    require_gpu()
+    w = synth.WORKLOADS["llama8b_1doc"]
+    N, Hq, Hkv, D = w["N"], w["Hq"] // w["P"], w["Hkv"] // w["P"], w["D"]
+    log(f"bwd llama8b_1doc N={N} whole tensors")
+    d, host = dev_inputs(N, Hq, Hkv, D, w["index"], torch.bfloat16, with_do=True)
+    o, lse = ul.attn_fwd(d["q"], d["k"], d["v"], None)
+    dq, dk, dv = ul.attn_bwd(d["q"], d["k"], d["v"], o, d["do"], lse, None)
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd(*(host[x].double().numpy() for x in ("q", "k", "v", "do")), None)
+    got = {"o": np64(o), "lse": np64(lse), "dq": np64(dq), "dk": np64(dk), "dv": np64(dv)}
+    err = {x: max_abs(got[x], ref[x]) for x in got}
+    log(f"bwd llama8b_1doc whole tensors: {err}")
+    for x in ("o", "dq", "dk", "dv"):
+        assert err[x] <= TOL_OUT, (x, err[x])
+    assert err["lse"] <= TOL_LSE
 
 
 def test_peaked_softmax_gradients():
