@@ -86,7 +86,10 @@ def test_full_path(name):
     pos_o = None if name == "million" else pos  # million: one document (ids 0..N-1)
     qf, k64, v64, dof = _host(r)
     rng = np.random.Generator(np.random.PCG64(11))
-    rows = np.unique(np.r_[0:16, N - 16:N, rng.integers(0, N, 16), 63, 64, 65, 4095, 4096])
+    # first and last 64 rows, rows on both sides of key-tile (64), work-group (64 tokens at 4 heads) and
+    # larger power-of-two boundaries, and 112 random rows (about 256 in all)
+    edges = [b + d for b in (64, 128, 4096, 65536, N // 2) for d in (-1, 0, 1) if 0 <= b + d < N]
+    rows = np.unique(np.r_[0:64, N - 64:N, edges, rng.integers(0, N, 112)])
     log(f"path {name}: oracle forward rows")
     rr, eo, el = oracle.attn_fwd_rows(qf, k64, v64, pos_o, rows)
     ri = torch.from_numpy(rr).to("cuda:0")
