@@ -51,6 +51,12 @@ typedef enum {
 
 typedef enum { UL_F32 = 0, UL_BF16 = 1 } ul_dtype;
 
+/* Largest N the fp32 attention calls accept.  Their kernels are small-case
+ * checks (one thread per query row, visiting its keys one after another), so
+ * their run time grows as N^2 with no MFMA; larger N is refused with
+ * UL_ERR_UNSUPPORTED before anything is enqueued. */
+#define UL_F32_MAX_N 65536
+
 /*
  * Step 1, seq->head exchange of rank `rank` (pages: nmedialink.com
  * "Ulysses的工作原理" steps 1 and 3; explore.n1n.ai "核心机制" steps 1 and 3).
@@ -124,9 +130,12 @@ size_t ul_attn_workspace_bytes(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, ul
  * bf16 inputs are multiplied on MFMA with fp32 accumulation and fp32 softmax;
  * the probabilities are rounded to bf16 before the P.V product.
  * Errors: UL_ERR_ARG for N < 1, Hq < 1, Hkv < 1, Hq % Hkv != 0, null or
- * misaligned pointer, workspace too small, non-finite or non-positive scale;
+ * misaligned pointer, workspace too small, non-finite or non-positive scale,
+ * an output or the workspace overlapping any other buffer (position_ids
+ * included: the document bounds are computed into the workspace from it);
  * UL_ERR_UNSUPPORTED for D not in {64, 128}, dtype not in {UL_F32, UL_BF16},
- * or (bf16) a group size Hq/Hkv that is not a power of two up to 16.
+ * (bf16) a group size Hq/Hkv that is not a power of two up to 16, or (fp32)
+ * N > UL_F32_MAX_N.
  */
 ul_status ul_attn_fwd(const void *q, const void *k, const void *v, const int32_t *position_ids,
                       void *o, float *lse, int64_t N, int32_t Hq, int32_t Hkv, int32_t D,

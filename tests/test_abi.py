@@ -78,10 +78,10 @@ def test_doc_bounds_rejections():
 
 def test_workspace_is_linear_in_n():
     lib = ul.load()
-    for dt in (ul.UL_BF16, ul.UL_F32):
+    for dt, n in ((ul.UL_BF16, 1 << 16), (ul.UL_F32, 1 << 15)):
         for bwd in (0, 1):
-            w1 = lib.ul_attn_workspace_bytes(1 << 16, 4, 1, 128, dt, bwd)
-            w2 = lib.ul_attn_workspace_bytes(1 << 17, 4, 1, 128, dt, bwd)
+            w1 = lib.ul_attn_workspace_bytes(n, 4, 1, 128, dt, bwd)
+            w2 = lib.ul_attn_workspace_bytes(2 * n, 4, 1, 128, dt, bwd)
             assert w1 > 0 and abs(w2 - 2 * w1) <= 4096
     # rejected shapes report 0
     assert lib.ul_attn_workspace_bytes(1024, 6, 4, 128, ul.UL_BF16, 0) == 0
@@ -227,3 +227,65 @@ def test_loss_rejections_cpu():
     assert ce(dl=E, tc=F, dloss=float("inf")) == ul.UL_ERR_ARG
     assert ce(dl=E, tc=E + 64) == ul.UL_ERR_ARG                # total_count inside dlogits
     assert ce(dl=C, tc=F) == ul.UL_ERR_ARG                     # dlogits overlaps loss_tok
+
+
+UL_F32_MAX_N = 65536  # include/ul.h
+
+
+def test_header_states_the_fp32_limit():
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+UL_F32_MAX_N\s+%d\b" % UL_F32_MAX_N, text)
+
+
+def test_fp32_attention_refuses_large_n_before_enqueueing():
+    """The fp32 kernels visit keys one after another per query row; a large N
+    is refused up front (pointers are fake: a refusal enqueues nothing)."""
+    lib = ul.load()
+    big = UL_F32_MAX_N + 64
+    assert lib.ul_attn_workspace_bytes(UL_F32_MAX_N, 8, 8, 64, ul.UL_F32, 0) > 0
+    assert lib.ul_attn_workspace_bytes(big, 8, 8, 64, ul.UL_F32, 0) == 0
+    assert lib.ul_attn_workspace_bytes(big, 8, 8, 64, ul.UL_BF16, 0) > 0
+    assert _fwd(lib, N=big, dt=ul.UL_F32) == ul.UL_ERR_UNSUPPORTED
+    assert "fp32" in _err() and str(UL_F32_MAX_N) in _err()
+    assert lib.ul_attn_bwd(A, B, C, D_, E, F, None, G_, H_, I_, big, 4, 1, 128, 0.1, ul.UL_F32, J, 1 << 40,
+                           None) == ul.UL_ERR_UNSUPPORTED
+    big_r = 8 * (UL_F32_MAX_N // 8 + 8)
+    assert lib.ul_rank_attn_fwd(A, B, C, None, D_, E, big_r, 32, 8, 128, 8, 0, 1, 0.1, ul.UL_F32, F, 1 << 40,
+                                None) == ul.UL_ERR_UNSUPPORTED
+    assert lib.ul_rank_attn_bwd(A, B, C, D_, E, F, None, G_, H_, I_, big_r, 32, 8, 128, 8, 0, 1, 0.1, ul.UL_F32,
+                                J, 1 << 40, None) == ul.UL_ERR_UNSUPPORTED
+    assert lib.ul_rank_workspace_bytes(big_r, 32, 8, 128, 8, 1, ul.UL_F32, 1) == 0
+
+
+def test_position_ids_may_not_alias_outputs_or_workspace():
+    """The document-bounds kernels read position_ids while writing the
+    workspace; an alias with the workspace or an output is refused."""
+    lib = ul.load()
+    N = 64
+    # forward: workspace F, outputs o = D_, lse = E
+    for pos, what in ((F, "ws"), (F + 128, "ws"), (D_, "o"), (E + 64, "lse")):
+        assert _fwd(lib, pos=pos) == ul.UL_ERR_ARG, what
+        assert "position_ids" in _err() and what in _err()
+    assert _fwd(lib, pos=A) != ul.UL_ERR_ARG or "position_ids" not in _err()  # reading an input is fine
+
+    def bwd(pos):
+        return lib.ul_attn_bwd(A, B, C, D_, E, F, pos, G_, H_, I_, N, 4, 1, 128, 0.1, ul.UL_BF16, J, 1 << 30, None)
+
+    for pos, what in ((J, "ws"), (G_ + 256, "dq"), (H_, "dk"), (I_ + 4, "dv")):
+        assert bwd(pos) == ul.UL_ERR_ARG, what
+        assert "position_ids" in _err() and what in _err()
+
+    def rfwd(pos):
+        return lib.ul_rank_attn_fwd(A, B, C, pos, D_, E, N, 32, 8, 128, 8, 0, 1, 0.1, ul.UL_BF16, F, 1 << 30, None)
+
+    for pos, what in ((F, "ws"), (D_ + 16, "o_seq"), (E, "lse")):
+        assert rfwd(pos) == ul.UL_ERR_ARG, what
+        assert "position_ids" in _err() and what in _err()
+
+    def rbwd(pos):
+        return lib.ul_rank_attn_bwd(A, B, C, D_, E, F, pos, G_, H_, I_, N, 32, 8, 128, 8, 0, 1, 0.1, ul.UL_BF16,
+                                    J, 1 << 30, None)
+
+    for pos, what in ((J + 512, "ws"), (G_, "dq_seq"), (H_, "dk_seq"), (I_, "dv_seq")):
+        assert rbwd(pos) == ul.UL_ERR_ARG, what
+        assert "position_ids" in _err() and what in _err()

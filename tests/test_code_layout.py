@@ -7,6 +7,10 @@ slower than at 24 (identical loop code).  Any change to a prologue moves the
 loop; this test compiles attn_bwd.hip for gfx950 with the library's flags,
 disassembles the device code and checks that the loops still start where the
 padding intends, so such a change cannot slip in unnoticed.
+
+The offsets are a performance guard, not a functional property: they hold for
+the compiler they were measured with (MEASURED_WITH).  With another compiler
+the test is skipped and reports the offsets it found instead of failing.
 """
 
 import os
@@ -20,6 +24,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "ulysses_sequence_parallelism_ul_amd", "csrc", "attn_bwd.hip")
 OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
 WANT = {"dkdv_kernelILi128": 40, "dq_kernelILi128": 24}
+# `hipcc --version` of the toolchain the padding was measured with
+MEASURED_WITH = "roc-7.2.0 26014 7b800a19466229b8479a78de19143dc33c3ab9b5"
 
 
 def _loop_offsets(dis_lines):
@@ -54,10 +60,14 @@ def test_backward_tile_loops_start_at_their_padded_offsets(tmp_path):
     if not os.path.exists(OBJDUMP) and shutil.which("llvm-objdump") is None:
         pytest.skip("llvm-objdump not available")
     objdump = OBJDUMP if os.path.exists(OBJDUMP) else shutil.which("llvm-objdump")
+    version = subprocess.run([hipcc, "--version"], capture_output=True, text=True).stdout
     obj = str(tmp_path / "attn_bwd_device.o")
     flags = [f for f in B.HIPCC_FLAGS if f != "-fPIC"]
     r = subprocess.run([hipcc] + flags + ["--cuda-device-only", "--no-gpu-bundle-output", "-c", SRC, "-o", obj],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     dis = subprocess.run([objdump, "-d", obj], capture_output=True, text=True, check=True).stdout.splitlines()
-    assert _loop_offsets(dis) == WANT
+    got = _loop_offsets(dis)
+    if MEASURED_WITH not in version:
+        pytest.skip(f"padding measured with {MEASURED_WITH}; this compiler places the loops at {got} (want {WANT})")
+    assert got == WANT

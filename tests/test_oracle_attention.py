@@ -133,6 +133,55 @@ def test_softmax_rows_sum_to_one_and_respect_mask():
             assert np.all(P[i, start[i]:i + 1] > 0)
 
 
+def _brute_probs(q, k, pos, scale, h, G):
+    """P[i, j] of query head h from scalar loops: exp of the scaled logit over
+    the sum of exp over the keys visible to i (tiny N only)."""
+    N, _, D = q.shape
+    doc, d = [], 0
+    for t in range(N):
+        if t > 0 and pos[t] == 0:
+            d += 1
+        doc.append(d)
+    P = np.zeros((N, N))
+    for i in range(N):
+        js = [j for j in range(N) if j <= i and doc[j] == doc[i]]
+        w = {j: math.exp(scale * sum(q[i, h, x] * k[j, h // G, x] for x in range(D))) for j in js}
+        tot = sum(w.values())
+        for j in js:
+            P[i, j] = w[j] / tot
+    return P
+
+
+def test_attn_probs_values():
+    """Every element of P against scalar loops, at a group size where h // G
+    and h % Hkv pick different KV heads and with a non-default scale; then
+    P V and the diagonal's log-probability against the forward's O and LSE
+    (log P_ii = scale q_i.k_i - LSE_i)."""
+    N, Hq, Hkv, D, sc = 23, 4, 2, 3, 0.37
+    q, k, v = _rand((N, Hq, D), 40, 1.5), _rand((N, Hkv, D), 41, 1.5), _rand((N, Hkv, D), 42)
+    pos = synth.position_ids_from_lengths([6, 1, 9, 7])
+    o, lse = oracle.attn_fwd(q, k, v, pos, sc, block=5)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        P = oracle.attn_probs(q, k, pos, sc, head=h)
+        np.testing.assert_allclose(P, _brute_probs(q, k, pos, sc, h, Hq // Hkv), rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(P @ v[:, g, :], o[:, h, :], rtol=1e-12, atol=1e-13)
+        diag = sc * np.einsum("nd,nd->n", q[:, h, :], k[:, g, :]) - np.log(np.diag(P))
+        np.testing.assert_allclose(diag, lse[h], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", ["one_document", "two_documents"])
+def test_attn_probs_golden_two_tokens(case):
+    """The hand-derived probabilities of the two-token example: one document
+    gives P_1 = [1/4, 3/4], two documents the identity."""
+    with open(os.path.join(GOLDEN, "attn_two_tokens.json")) as f:
+        g = json.load(f)
+    q = np.array([g["q0"], math.log(3.0)]).reshape(2, 1, 1)
+    k = np.array([0.0, 1.0]).reshape(2, 1, 1)
+    P = oracle.attn_probs(q, k, g[case]["position_ids"], 1.0)
+    np.testing.assert_allclose(P, np.array(g[case]["p"]), rtol=1e-15, atol=1e-15)
+
+
 def test_first_row_of_every_document_returns_its_v_row():
     N, Hq, Hkv, D = 50, 4, 2, 5
     q, k, v = _rand((N, Hq, D), 10), _rand((N, Hkv, D), 11), _rand((N, Hkv, D), 12)

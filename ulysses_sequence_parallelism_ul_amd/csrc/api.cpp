@@ -63,6 +63,17 @@ ul_status check_bufs(const Buf* b, int count, uintptr_t align) {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// position_ids (N int32, optional) is read by the document-bounds kernels
+// while they write the workspace, and must not alias that or any output.
+ul_status check_position_ids(const int32_t* pos, int64_t N, const Buf* outs, int count) {
+  if (pos == nullptr) return UL_OK;
+  if (!aligned(pos, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  for (int i = 0; i < count; ++i)
+    if (overlap(pos, (size_t)N * 4, outs[i].p, outs[i].n))
+      return fail(UL_ERR_ARG, "position_ids and %s overlap", outs[i].name);
+  return UL_OK;
+}
+
 ul_status check_relayout(const void* src, void* dst, bool seq_to_head, int64_t N, int32_t H, int32_t D, int32_t P,
                          int32_t rank, ul_dtype dt) {
   if (dt != UL_BF16 && dt != UL_F32) return fail(UL_ERR_UNSUPPORTED, "dtype %d is not UL_F32 or UL_BF16", (int)dt);
@@ -85,6 +96,10 @@ ul_status check_attn_shapes(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, float
   if (Hq < 1 || Hkv < 1) return fail(UL_ERR_ARG, "Hq=%d and Hkv=%d must be >= 1", Hq, Hkv);
   if (Hq % Hkv != 0) return fail(UL_ERR_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (D != 64 && D != 128) return fail(UL_ERR_UNSUPPORTED, "head dim D=%d is not 64 or 128", D);
+  // the fp32 kernels are small-case checks (one thread per query row, keys in
+  // series): their time grows as N^2, so large N is refused rather than run
+  if (dt == UL_F32 && N > UL_F32_MAX_N)
+    return fail(UL_ERR_UNSUPPORTED, "fp32 attention is limited to N <= %d, got N=%lld", UL_F32_MAX_N, (long long)N);
   if (dt == UL_BF16 && !(is_pow2(Hq / Hkv) && Hq / Hkv <= 16))
     return fail(UL_ERR_UNSUPPORTED, "bf16 attention needs a power-of-two group size <= 16, got %d", Hq / Hkv);
   if ((int64_t)N * (Hq / Hkv) > 0x7fffffffLL) return fail(UL_ERR_ARG, "N * Hq / Hkv must be < 2^31");
@@ -272,7 +287,8 @@ ul_status ul_attn_fwd(const void* q, const void* k, const void* v, const int32_t
     for (int j = 0; j < 6; ++j)
       if (i != j && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
         return fail(UL_ERR_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
-  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  st = check_position_ids(position_ids, N, bufs + 3, 3);
+  if (st != UL_OK) return st;
   if (ws_bytes < L.total) return fail(UL_ERR_ARG, "workspace of %zu bytes is smaller than %zu", ws_bytes, L.total);
   hipStream_t s = (hipStream_t)stream;
   char* w = static_cast<char*>(ws);
@@ -312,7 +328,8 @@ ul_status ul_attn_bwd(const void* q, const void* k, const void* v, const void* o
     for (int j = 0; j < 10; ++j)
       if (i != j && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
         return fail(UL_ERR_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
-  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  st = check_position_ids(position_ids, N, bufs + 6, 4);
+  if (st != UL_OK) return st;
   if (ws_bytes < L.total) return fail(UL_ERR_ARG, "workspace of %zu bytes is smaller than %zu", ws_bytes, L.total);
   hipStream_t s = (hipStream_t)stream;
   char* w = static_cast<char*>(ws);
@@ -366,7 +383,8 @@ ul_status ul_rank_attn_fwd(const void* q_seq, const void* k_seq, const void* v_s
     for (int j = 0; j < 6; ++j)
       if (i != j && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
         return fail(UL_ERR_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
-  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  st = check_position_ids(position_ids, N, bufs + 3, 3);
+  if (st != UL_OK) return st;
   if (ws_bytes < W.total) return fail(UL_ERR_ARG, "workspace of %zu bytes is smaller than %zu", ws_bytes, W.total);
 
   hipStream_t s = (hipStream_t)stream;
@@ -426,7 +444,8 @@ ul_status ul_rank_attn_bwd(const void* q_seq, const void* k_seq, const void* v_s
     for (int j = 0; j < 10; ++j)
       if (i != j && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
         return fail(UL_ERR_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
-  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  st = check_position_ids(position_ids, N, bufs + 6, 4);
+  if (st != UL_OK) return st;
   if (ws_bytes < W.total) return fail(UL_ERR_ARG, "workspace of %zu bytes is smaller than %zu", ws_bytes, W.total);
 
   hipStream_t s = (hipStream_t)stream;

@@ -28,9 +28,6 @@ namespace ul {
 namespace {
 
 constexpr int kCeThreads = 1024;
-#ifndef UL_CE_RESIDENT
-#define UL_CE_RESIDENT 1  // 0: always stream the rows (two reads), for comparison
-#endif
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -249,15 +246,11 @@ template <typename T>
 hipError_t launch_ce_pick(const T* logits, const int32_t* labels, float* loss_tok, T* dlogits,
                           const int64_t* total_count, float dloss, int64_t Tn, int V, int ign, hipStream_t s) {
   const int per_thread = (V / Chunk<T>::E + kCeThreads - 1) / kCeThreads;
-  if (UL_CE_RESIDENT) {
-    if (per_thread <= 2) return launch_ce_t<T, 2>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
-    if (per_thread <= 4) return launch_ce_t<T, 4>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
-    if (per_thread <= 8) return launch_ce_t<T, 8>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
-    if (per_thread <= 16)
-      return launch_ce_t<T, 16>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
-    if (per_thread <= 20)
-      return launch_ce_t<T, 20>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
-  }
+  if (per_thread <= 2) return launch_ce_t<T, 2>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
+  if (per_thread <= 4) return launch_ce_t<T, 4>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
+  if (per_thread <= 8) return launch_ce_t<T, 8>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
+  if (per_thread <= 16) return launch_ce_t<T, 16>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
+  if (per_thread <= 20) return launch_ce_t<T, 20>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
   return launch_ce_t<T, 0>(logits, labels, loss_tok, dlogits, total_count, dloss, Tn, V, ign, s);
 }
 
