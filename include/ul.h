@@ -105,6 +105,23 @@ ul_status ul_doc_bounds(const int32_t *position_ids, int32_t *doc_start, int32_t
                         int64_t N, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * ul_doc_bounds without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same inputs, outputs and results as ul_doc_bounds; the
+ * scan partials live in a fixed device array of the library (512 KiB on every
+ * GPU it runs on, held until the process ends), so N is limited to
+ * UL_DOC_BOUNDS_NOALLOC_MAX_N.  The call allocates nothing.  Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must not be issued.
+ * `stream` must belong to the current device.  Errors: as ul_doc_bounds, and
+ * UL_ERR_ARG for N > UL_DOC_BOUNDS_NOALLOC_MAX_N; UL_ERR_HIP if the array's
+ * device address cannot be obtained.
+ */
+#define UL_DOC_BOUNDS_NOALLOC_MAX_N (1 << 26)
+ul_status ul_doc_bounds_noalloc(const int32_t *position_ids, int32_t *doc_start, int32_t *doc_end,
+                                int64_t N, void *stream);
+
+/*
  * Workspace bytes ul_attn_fwd (for_bwd = 0) or ul_attn_bwd (for_bwd = 1)
  * needs for these shapes.  Linear in N (never N^2).  Returns 0 for shapes
  * the calls would reject.

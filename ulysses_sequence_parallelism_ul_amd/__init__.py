@@ -23,6 +23,7 @@ __all__ = [
     "seq_to_head",
     "head_to_seq",
     "doc_bounds",
+    "doc_bounds_noalloc",
     "attn_workspace_bytes",
     "attn_fwd",
     "attn_bwd",
@@ -66,6 +67,7 @@ SIGNATURES = {
     "ul_head_to_seq": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P]),
     "ul_doc_bounds_workspace_bytes": (_SZ, [_I64]),
     "ul_doc_bounds": (_I32, [_P, _P, _P, _I64, _P, _SZ, _P]),
+    "ul_doc_bounds_noalloc": (_I32, [_P, _P, _P, _I64, _P]),
     "ul_attn_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32]),
     "ul_attn_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
     "ul_attn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
@@ -216,6 +218,23 @@ def doc_bounds(position_ids, N=None, device=None):
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device)
     _check(lib.ul_doc_bounds(pptr, ds.data_ptr(), de.data_ptr(), N, ws.data_ptr(), wsb, _stream(device)))
     return ds, de
+
+
+def doc_bounds_noalloc(position_ids, doc_start, doc_end, N=None):
+    """ul_doc_bounds_noalloc into caller-allocated int32 [N] outputs (nothing is allocated)."""
+    lib = load()
+    pptr = None
+    if position_ids is not None:
+        if position_ids.dtype != torch.int32:
+            raise TypeError("position_ids must be int32")
+        N = position_ids.numel()
+        pptr = _dev(position_ids, "position_ids")
+    for t, name in ((doc_start, "doc_start"), (doc_end, "doc_end")):
+        if t.dtype != torch.int32 or t.numel() != N:
+            raise ValueError(f"{name} must be int32 with N={N} elements")
+    _check(lib.ul_doc_bounds_noalloc(pptr, _dev(doc_start, "doc_start"), _dev(doc_end, "doc_end"), N,
+                                     _stream(doc_start.device)))
+    return doc_start, doc_end
 
 
 def attn_workspace_bytes(N, Hq, Hkv, D, dtype, for_bwd):

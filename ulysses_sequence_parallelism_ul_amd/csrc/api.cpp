@@ -260,6 +260,24 @@ ul_status ul_doc_bounds(const int32_t* position_ids, int32_t* doc_start, int32_t
                     "doc_bounds launch");
 }
 
+ul_status ul_doc_bounds_noalloc(const int32_t* position_ids, int32_t* doc_start, int32_t* doc_end, int64_t N,
+                                void* stream) {
+  if (N < 1 || N > ul::kNoAllocMaxN)
+    return fail(UL_ERR_ARG, "N=%lld must be in [1, %lld] for the allocation-free document bounds", (long long)N,
+                (long long)ul::kNoAllocMaxN);
+  if (position_ids && !aligned(position_ids, 4)) return fail(UL_ERR_ARG, "position_ids is not 4-byte aligned");
+  Buf bufs[2] = {{doc_start, (size_t)N * 4, "doc_start"}, {doc_end, (size_t)N * 4, "doc_end"}};
+  ul_status st = check_bufs(bufs, 2, 4);
+  if (st != UL_OK) return st;
+  st = check_position_ids(position_ids, N, bufs, 2);
+  if (st != UL_OK) return st;
+  int32_t* scan = nullptr;
+  hipError_t e = ul::noalloc_scan_scratch(&scan);
+  if (e != hipSuccess) return hip_status(e, "scratch address lookup");
+  return hip_status(ul::launch_doc_bounds(position_ids, doc_start, doc_end, scan, (int)N, (hipStream_t)stream),
+                    "doc_bounds launch");
+}
+
 size_t ul_attn_workspace_bytes(int64_t N, int32_t Hq, int32_t Hkv, int32_t D, ul_dtype dt, int32_t for_bwd) {
   std::string saved = g_err;
   ul_status st = check_attn_shapes(N, Hq, Hkv, D, 1.0f, dt);

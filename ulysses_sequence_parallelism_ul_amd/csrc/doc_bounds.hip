@@ -12,6 +12,8 @@
 // attention.
 #include "ul_internal.h"
 
+#include <mutex>
+
 namespace ul {
 namespace {
 
@@ -118,7 +120,33 @@ __global__ void __launch_bounds__(kThreads) docb_scan(const int32_t* __restrict_
   }
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+
 }  // namespace
+
+// Scan partials of the allocation-free entry point: one array per GPU, held
+// until the process ends.  In host code `scratch` is only a stand-in for the
+// device symbol; its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever passed to a kernel.
+static __device__ __align__(256) int32_t scratch[2 * ((kNoAllocMaxN + kScanBlock - 1) / kScanBlock)];
+
+hipError_t noalloc_scan_scratch(int32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_doc_bounds(const int32_t* pos, int32_t* doc_start, int32_t* doc_end, int32_t* scan, int N,
                              hipStream_t s) {

@@ -24,6 +24,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kTB = 64;
 // Tokens per block of the document-bounds scan.
 constexpr int kScanBlock = 1024;
+// Largest N of the allocation-free document bounds (its scan partials live in
+// a fixed device array of 2 * N / kScanBlock int32, 512 KiB).
+constexpr int64_t kNoAllocMaxN = UL_DOC_BOUNDS_NOALLOC_MAX_N;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -79,6 +82,9 @@ hipError_t launch_relayout(const void* src, void* dst, int64_t N, int H, int D, 
                            int elem_bytes, bool seq_to_head, hipStream_t s);
 hipError_t launch_doc_bounds(const int32_t* pos, int32_t* doc_start, int32_t* doc_end,
                              int32_t* scan_scratch, int N, hipStream_t s);
+// Device address, on the current device, of the fixed scan-partials array of
+// the allocation-free document bounds (looked up once per device).
+hipError_t noalloc_scan_scratch(int32_t** out);
 // [cols][D] bf16 view (column c -> token c >> lgG, head (hk << lgG) + (c & (G-1)) of a
 // [N][H][D] tensor) -> blocked transpose [Hkv][ceil(ncols / kTB)][D][kTB], zero-padded.
 hipError_t launch_transpose_blocked(const bf16* src, bf16* dst, int64_t ncols, int H, int Hkv, int lgG, int D,
