@@ -156,12 +156,21 @@ struct DkvCfg {
   static_assert(RED_BYTES <= SMEM, "reduction buffer must fit in LDS");
 };
 
+// Query-tile windows: the tiles a key block sees are split at multiples of
+// `win_tiles`.  One launch (win < 0) takes every key block's tiles inside the
+// window that holds its diagonal tile and writes dK / dV; then one launch per
+// later window takes the key blocks that see that window from below and adds
+// to dK / dV.  All work-groups of such a launch sweep the same window from its
+// top, so the ones resident together stay within a few tiles of each other
+// and share the window's Q / dO tiles in L2 (one sweep over the whole
+// sequence drifts apart by more than the L2 holds).
 template <int D>
 __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ doc_start, const int32_t* __restrict__ doc_end, const int32_t* __restrict__ order,
-    float* __restrict__ dk, float* __restrict__ dv, int N, int Hkv, int lgG, float sl2, float scale) {
+    float* __restrict__ dk, float* __restrict__ dv, int N, int Hkv, int lgG, float sl2, float scale, int win_tiles,
+    int win) {
   using C = DkvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   UL_CODE_PAD(13);  // tile loop at 40 bytes into a 64-byte line (D = 128)
@@ -176,8 +185,14 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   const int kb_last = min(N - 1, kb0 + C::BNK - 1);
   const int row_end = doc_end[kb_last];
   const int de0 = doc_end[kb0];  // rows after it belong to later documents than key kb0
-  const int tq_lo = (int)(((int64_t)kb0 << lgG) / C::BQ);
-  const int tq_hi = (int)((((int64_t)(row_end + 1) << lgG) - 1) / C::BQ);
+  // every query tile that sees a key of this block, then this launch's part of it
+  const int tq_first = (int)(((int64_t)kb0 << lgG) / C::BQ);
+  const int tq_last = (int)((((int64_t)(row_end + 1) << lgG) - 1) / C::BQ);
+  const int diag_win = tq_first / win_tiles;
+  const bool accumulate = win >= 0;
+  if (accumulate && (diag_win >= win || tq_last < win * win_tiles)) return;  // nothing here (uniform)
+  const int tq_lo = accumulate ? win * win_tiles : tq_first;
+  const int tq_hi = min(tq_last, (accumulate ? win : diag_win) * win_tiles + win_tiles - 1);
   const int key = kb0 + kbw * 32 + lc;
   const bool kvalid = key < N;
   // query column c sees this lane's key iff key <= row(c) <= doc_end[key], i.e.
@@ -449,6 +464,10 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
           a[e] = dkt[db][j * 4 + e] * scale;
           bb[e] = dvt[db][j * 4 + e];
         }
+        if (accumulate) {  // the earlier windows' sums, in window order
+          a += *reinterpret_cast<const f32x4*>(dk + base + d);
+          bb += *reinterpret_cast<const f32x4*>(dv + base + d);
+        }
         *reinterpret_cast<f32x4*>(dk + base + d) = a;
         *reinterpret_cast<f32x4*>(dv + base + d) = bb;
       }
@@ -611,6 +630,10 @@ int ilog2_pow2(int x) {
   return l;
 }
 
+// Query tiles per dK / dV window (2048 tiles of 64 columns: 32768 tokens of a
+// 4-head group, 64 MiB of Q and dO tiles).
+constexpr int kDkvWindowTiles = 2048;
+
 }  // namespace
 
 hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o, const bf16* dout,
@@ -646,16 +669,23 @@ hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, con
     if (e != hipSuccess) return e;
   }
   {
+    // the diagonal windows first (they write dK / dV), then every later
+    // window in increasing order (each adds to dK / dV)
     const dim3 grid((unsigned)((int64_t)nkb * Hkv));
-    TimedLaunch timer("attn_bwd_dkdv", s);
-    if (D == 128)
-      hipLaunchKernelGGL(dkdv_kernel<128>, grid, dim3(DkvCfg<128>::kThreads), 0, s, q, k, v, dout, lse, delta,
-                         doc_start, doc_end, order_key, dk, dv, N, Hkv, lgG, sl2, scale);
-    else
-      hipLaunchKernelGGL(dkdv_kernel<64>, grid, dim3(DkvCfg<64>::kThreads), 0, s, q, k, v, dout, lse, delta,
-                         doc_start, doc_end, order_key, dk, dv, N, Hkv, lgG, sl2, scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const int ntiles = (int)((NG + kColTile - 1) / kColTile);
+    const int nwin = (ntiles + kDkvWindowTiles - 1) / kDkvWindowTiles;
+    for (int win = -1; win < nwin; ++win) {
+      if (win == 0) continue;  // no key block sees window 0 from below
+      TimedLaunch timer("attn_bwd_dkdv", s);
+      if (D == 128)
+        hipLaunchKernelGGL(dkdv_kernel<128>, grid, dim3(DkvCfg<128>::kThreads), 0, s, q, k, v, dout, lse, delta,
+                           doc_start, doc_end, order_key, dk, dv, N, Hkv, lgG, sl2, scale, kDkvWindowTiles, win);
+      else
+        hipLaunchKernelGGL(dkdv_kernel<64>, grid, dim3(DkvCfg<64>::kThreads), 0, s, q, k, v, dout, lse, delta,
+                           doc_start, doc_end, order_key, dk, dv, N, Hkv, lgG, sl2, scale, kDkvWindowTiles, win);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   {
     const dim3 grid((unsigned)((int64_t)ncb * Hkv)), block(NW * 64);
