@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     int win) {
   using C = DkvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  UL_CODE_PAD(13);  // tile loop at 40 bytes into a 64-byte line (D = 128)
+  UL_CODE_PAD(8);  // tile loop at 40 bytes into a 64-byte line (D = 128)
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
   const int kbw = w & 3;   // this wave's 32-key block
   const int qh = w >> 2;   // this wave's half of every query tile
