@@ -9,12 +9,19 @@ TOL_OUT = 2e-2
 TOL_LSE = 1e-3
 
 
-def grad_bar(ref):
-    """Gradient bar: 2e-2 absolute while |ref| <= 8 (the regime of the 4 q / 1 KV
-    workloads), then the same relative error (2e-2 / 8 = 2.5e-3, about one bf16
-    half-ulp of the probabilities) for larger gradients, which arise with larger
-    query groups summing into one KV head."""
-    return TOL_OUT * max(1.0, float(np.abs(ref).max()) / 8.0)
+# bf16 gradient cases held to a looser bar than the absolute 2e-2, each with the
+# error measured on MI355X.  Key: the test's case tuple and the tensor.
+GRAD_BAR_DEVIATIONS = {
+    # 16 query heads on one KV head: dV sums 16 heads' bf16-rounded probabilities
+    # into values up to 15.9; measured max|err| 2.16e-2 (1.4e-3 of max|dV|).
+    # Held to 2.5e-3 of max|dV|.
+    ("bwd_small", 2048, 16, 1, 128, "random", "dv"): 4e-2,
+}
+
+
+def grad_bar(*case):
+    """The bar of a bf16 gradient: the absolute 2e-2, unless the case is listed above."""
+    return GRAD_BAR_DEVIATIONS.get(case, TOL_OUT)
 
 
 def require_gpu():

@@ -153,3 +153,68 @@ def test_power_clock_context_scales_the_peak_by_the_clock():
     assert out["dominant_frac_at_clock"] == pytest.approx(1100.0 / 1875.0)
     out = bench.power_clock_context({"samples": 0, "gfx_clock_mhz": None, "board_power_w": None}, roof)
     assert "mfma_peak_at_clock_tflops" not in out
+
+
+def test_cpu_host_info_and_extrapolation():
+    info = bench.cpu_host_info()
+    assert info["affinity_cores"] >= 1
+    assert set(info) == {"cpu_model", "affinity_cores", "blas"}
+    # 2 s on 32768 tokens -> 2 * 32^2 s on 1M tokens, labelled as an extrapolation
+    ex = bench.extrapolate_oracle(2.0, 32768, 1 << 20, 3.9407e15)
+    assert ex["extrapolated"] is True
+    assert ex["seconds"] == pytest.approx(2.0 * 1024)
+    assert ex["value"] == pytest.approx(3.9407e15 / 2048.0 / 1e12)
+
+
+def test_traffic_report_calibrates_with_the_plain_copy(tmp_path):
+    kib, mib = 1024.0, 256
+    known = mib * 2**20
+
+    def counters(name, copy, dkdv):
+        return [dict(Kernel_Name="void at::native::vectorized_elementwise_kernel<4, MulFunctor<float>>",
+                     Counter_Name=name, Counter_Value=copy / kib),
+                dict(Kernel_Name="dkdv_kernel<128>", Counter_Name=name, Counter_Value=dkdv / kib)]
+
+    fd, wd = tmp_path / "f", tmp_path / "w"
+    # FETCH_SIZE counts half of what the copy reads, WRITE_SIZE all of it
+    _write_csv(str(fd / "run_counter_collection.csv"), counters("FETCH_SIZE", known / 2, 1.0e12))
+    _write_csv(str(wd / "run_counter_collection.csv"), counters("WRITE_SIZE", known, 1.0e9))
+    text = bench.traffic_report("million", str(fd), str(wd), cal_mib=mib)
+    assert "plain copy of known size in the same run" in text and "FETCH_SIZE x 2.000, WRITE_SIZE x 1.000" in text
+    import json
+    import re
+
+    rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))["kernels"]["dkdv_kernel"]
+    assert rec["fetch_bytes"] == pytest.approx(2.0e12) and rec["write_bytes"] == pytest.approx(1.0e9)
+
+
+def test_counter_report_request_sizes_and_mfma_counts(tmp_path):
+    w = synth.WORKLOADS["million"]
+    pos = synth.workload_positions("million")
+    tiles = bench.attention_tile_counts(pos, 4, w["N"])
+    # one document of 2^20 tokens: column blocks cb see key tiles 0..cb, key blocks kb see 65536 - 8 kb tiles
+    ncb, nkb = (w["N"] * 4) // 256, w["N"] // 128
+    assert tiles["fwd_dq"] == ncb * (ncb + 1) // 2
+    assert tiles["dkdv"] == sum(65536 - 8 * kb for kb in range(nkb))
+    rows = []
+
+    def add(kern, c, v, n=1):
+        for _ in range(n):
+            rows.append(dict(Kernel_Name=kern, Counter_Name=c, Counter_Value=v / n))
+
+    # relayout: 1000 x 128-byte and 10 x 32-byte reads, 500 x 64-byte writes
+    add("relayout_kernel", "TCC_EA0_RDREQ_sum", 1010, 8)
+    add("relayout_kernel", "TCC_EA0_RDREQ_32B_sum", 10, 8)
+    add("relayout_kernel", "TCC_BUBBLE_sum", 1000, 8)
+    add("relayout_kernel", "TCC_EA0_WRREQ_sum", 500, 8)
+    add("relayout_kernel", "TCC_EA0_WRREQ_64B_sum", 500, 8)
+    pred = tiles["dkdv"] * 256
+    add("dkdv_kernel<128>", "SQ_INSTS_MFMA", pred, 32)
+    add("dkdv_kernel<128>", "SQ_INSTS_VALU_MFMA_MOPS_BF16", pred * 64, 32)
+    _write_csv(str(tmp_path / "a" / "run_counter_collection.csv"), rows)
+    text = bench.counter_report("million", [str(tmp_path / "a")])
+    assert f"| relayout_kernel | 8 | 1010 | 10 | 0 | 1000 | - | {(1000 * 128 + 320) / 2**30:.3f} |" in text
+    assert f"| relayout_kernel | 8 | 500 | 500 | - | {500 * 64 / 2**30:.3f} |" in text
+    line = [ln for ln in text.splitlines() if ln.startswith("| dkdv_kernel |")][0]
+    cells = [c.strip() for c in line.strip("|").split("|")]
+    assert cells[1] == "32" and cells[4] == "1.0000" and cells[7] == "1.0000"

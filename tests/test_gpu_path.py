@@ -6,7 +6,8 @@ Checks: exchanges bit-exact on full tensors against a torch slice (an
 independent library routine) and on sampled rows against the oracle; forward
 and dQ on sampled rows against the oracle; dK/dV on the last 64 keys of each
 of the first three documents against the oracle; per-document dK/dV sums; the
-Q = 0 closed forms at N = 1M; determinism; and, for the training share, every
+Q = 0 and K = 0 closed forms at N = 1M (the latter on whole dK / dV tensors);
+determinism; and, for the training share, every
 document's O, LSE, dQ, dK and dV on whole tensors against the oracle run per
 document.
 """
@@ -162,6 +163,68 @@ def test_million_zero_queries_closed_forms():
     g = r["do"].double().sum(dim=1) / idx[:, None]          # group sum of dO_i / (i+1)
     dv_ref = torch.flip(torch.cumsum(torch.flip(g, [0]), dim=0), [0])
     assert float((r["dv"][:, 0].double() - dv_ref).abs().max()) <= TOL_OUT
+
+
+@pytest.mark.timeout(300)
+def test_million_zero_keys_closed_forms():
+    """K = 0 over one 1M-token document with dO non-zero only on a few rows R
+    spread over the whole sequence, scaled by (i+1)/16 so that every such row
+    adds O(0.1) to the gradient of every key before it.  Then P_ij = 1/(i+1)
+    and, with n_i = i+1 and O_i = mean(V[0..i]):
+      dQ = 0,  dV_j = sum_{i in R, i >= j} sum_h dO_ih / n_i,
+      dK_j = scale sum_{i in R, i >= j} sum_h ((dO_ih . V_j) - dO_ih . O_i) Q_ih / n_i,
+    so dK (with non-zero Q) and dV are checked on whole tensors, including the
+    query rows far above each key's own window."""
+    require_gpu()
+    log("path million K=0, sparse dO")
+    N, Hq, D = 1 << 20, 4, 128
+    dev = torch.device("cuda:0")
+    scale = 1.0 / D ** 0.5
+    q = synth.device_normal((N, Hq, D), 9, 1, dev, torch.bfloat16)
+    v = synth.device_normal((N, 1, D), 9, 3, dev, torch.bfloat16)
+    k = torch.zeros((N, 1, D), dtype=torch.bfloat16, device=dev)
+    rows = sorted({0, 5, 1000, 32767, 32768, 40000, 65535, 65536, 100000, 131071, 262143, 262144, 300001,
+                   500000, 524288, 640000, 777777, 900000, 1000000, 1048575}
+                  | set(np.random.Generator(np.random.PCG64(9)).integers(0, N, 12).tolist()))
+    R = torch.tensor(rows, device=dev)
+    n_r = (R + 1).double()
+    do = torch.zeros((N, Hq, D), dtype=torch.bfloat16, device=dev)
+    do[R] = (synth.device_normal((len(rows), Hq, D), 9, 4, dev, torch.float32) * (n_r / 16.0)[:, None, None].float()
+             ).to(torch.bfloat16)
+    o, lse = ul.attn_fwd(q, k, v, None)
+    dq, dk, dv = ul.attn_bwd(q, k, v, o, do, lse, None)
+    torch.cuda.synchronize()
+    idx = torch.arange(1, N + 1, device=dev, dtype=torch.float64)
+    mean = torch.cumsum(v[:, 0].double(), dim=0) / idx[:, None]
+    for h in range(Hq):
+        assert float((o[:, h].double() - mean).abs().max()) <= TOL_OUT
+        assert float((lse[h].double() - torch.log(idx)).abs().max()) <= TOL_LSE
+    assert float(dq.abs().max()) == 0.0
+    # per row i of R: A = sum_h dO_ih Q_ih^T / n_i (so V_j A = sum_h (dO_ih . V_j) Q_ih / n_i),
+    # b = sum_h (dO_ih . O_i) Q_ih / n_i, g = sum_h dO_ih / n_i
+    qr, dor = q[R].double(), do[R].double()
+    A = torch.stack([dor[i].t().contiguous() @ qr[i] for i in range(len(rows))]) / n_r[:, None, None]
+    delta = (dor * mean[R][:, None, :]).sum(dim=2)
+    b = (delta[:, :, None] * qr).sum(dim=1) / n_r[:, None]
+    g = dor.sum(dim=1) / n_r[:, None]
+    # suffix sums over R; keys in (r_{k-1}, r_k] see rows r_k, r_{k+1}, ...
+    A_s = torch.flip(torch.cumsum(torch.flip(A, [0]), 0), [0])
+    b_s = torch.flip(torch.cumsum(torch.flip(b, [0]), 0), [0])
+    g_s = torch.flip(torch.cumsum(torch.flip(g, [0]), 0), [0])
+    dk_err = dv_err = 0.0
+    lo = 0
+    for kk, r in enumerate(rows):
+        vj = v[lo:r + 1, 0].double()
+        dk_ref = scale * (vj @ A_s[kk] - b_s[kk])
+        dk_err = max(dk_err, float((dk[lo:r + 1, 0].double() - dk_ref).abs().max()))
+        dv_err = max(dv_err, float((dv[lo:r + 1, 0].double() - g_s[kk]).abs().max()))
+        lo = r + 1
+    if lo < N:
+        dk_err = max(dk_err, float(dk[lo:].abs().max()))
+        dv_err = max(dv_err, float(dv[lo:].abs().max()))
+    log(f"  million K=0: max|dK - closed form| {dk_err:.3e}, max|dV - closed form| {dv_err:.3e}, "
+        f"max|dK| {float(dk.abs().max()):.3f}, max|dV| {float(dv.abs().max()):.3f}")
+    assert dk_err <= TOL_OUT and dv_err <= TOL_OUT
 
 
 @pytest.mark.timeout(300)
