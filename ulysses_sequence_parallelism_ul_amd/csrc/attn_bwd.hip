@@ -156,14 +156,18 @@ struct DkvCfg {
   static_assert(RED_BYTES <= SMEM, "reduction buffer must fit in LDS");
 };
 
-// Query-tile windows: the tiles a key block sees are split at multiples of
-// `win_tiles`.  One launch (win < 0) takes every key block's tiles inside the
-// window that holds its diagonal tile and writes dK / dV; then one launch per
-// later window takes the key blocks that see that window from below and adds
-// to dK / dV.  All work-groups of such a launch sweep the same window from its
-// top, so the ones resident together stay within a few tiles of each other
-// and share the window's Q / dO tiles in L2 (one sweep over the whole
-// sequence drifts apart by more than the L2 holds).
+// Query-tile windows: a key block whose tiles reach at least two windows of
+// `win_tiles` tiles beyond the window that holds its diagonal tile has them
+// split at the window bounds.  One launch (win < 0) takes every key block's
+// tiles inside its diagonal window (or all of them, for a key block that is
+// not split) and writes dK / dV; then one launch per later window takes the
+// split key blocks that see that window from below and adds to dK / dV.  All
+// work-groups of such a launch sweep the same window from its top, so the
+// ones resident together stay within a few tiles of each other and share the
+// window's Q / dO tiles in L2 (one sweep over a long document drifts apart by
+// more than the L2 holds).  Key blocks of shorter documents keep one sweep:
+// split, their few window parts would run as a short tail of mostly idle
+// launches.
 template <int D>
 __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -173,7 +177,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     int win) {
   using C = DkvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  UL_CODE_PAD(8);  // tile loop at 40 bytes into a 64-byte line (D = 128)
+  UL_CODE_PAD(5);  // tile loop at 40 bytes into a 64-byte line (D = 128)
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
   const int kbw = w & 3;   // this wave's 32-key block
   const int qh = w >> 2;   // this wave's half of every query tile
@@ -189,10 +193,11 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   const int tq_first = (int)(((int64_t)kb0 << lgG) / C::BQ);
   const int tq_last = (int)((((int64_t)(row_end + 1) << lgG) - 1) / C::BQ);
   const int diag_win = tq_first / win_tiles;
+  const bool split = tq_last / win_tiles - diag_win >= 2;
   const bool accumulate = win >= 0;
-  if (accumulate && (diag_win >= win || tq_last < win * win_tiles)) return;  // nothing here (uniform)
+  if (accumulate && (!split || diag_win >= win || tq_last < win * win_tiles)) return;  // nothing here (uniform)
   const int tq_lo = accumulate ? win * win_tiles : tq_first;
-  const int tq_hi = min(tq_last, (accumulate ? win : diag_win) * win_tiles + win_tiles - 1);
+  const int tq_hi = split ? min(tq_last, (accumulate ? win : diag_win) * win_tiles + win_tiles - 1) : tq_last;
   const int key = kb0 + kbw * 32 + lc;
   const bool kvalid = key < N;
   // query column c sees this lane's key iff key <= row(c) <= doc_end[key], i.e.
