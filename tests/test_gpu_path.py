@@ -165,31 +165,24 @@ def test_million_zero_queries_closed_forms():
     assert float((r["dv"][:, 0].double() - dv_ref).abs().max()) <= TOL_OUT
 
 
-@pytest.mark.timeout(300)
-def test_million_zero_keys_closed_forms():
-    """K = 0 over one 1M-token document with dO non-zero only on a few rows R
-    spread over the whole sequence, scaled by (i+1)/16 so that every such row
-    adds O(0.1) to the gradient of every key before it.  Then P_ij = 1/(i+1)
-    and, with n_i = i+1 and O_i = mean(V[0..i]):
+def _zero_keys_closed_forms(N, Hq, D, rows, seed):
+    """K = 0 over one N-token document (one KV head) with dO non-zero only on
+    the rows R, scaled by (i+1)/16 so that every such row adds O(0.1) to the
+    gradient of every key before it.  Then P_ij = 1/(i+1) and, with n_i = i+1
+    and O_i = mean(V[0..i]):
       dQ = 0,  dV_j = sum_{i in R, i >= j} sum_h dO_ih / n_i,
       dK_j = scale sum_{i in R, i >= j} sum_h ((dO_ih . V_j) - dO_ih . O_i) Q_ih / n_i,
     so dK (with non-zero Q) and dV are checked on whole tensors, including the
-    query rows far above each key's own window."""
-    require_gpu()
-    log("path million K=0, sparse dO")
-    N, Hq, D = 1 << 20, 4, 128
+    query rows far above each key's own window of query tiles."""
     dev = torch.device("cuda:0")
     scale = 1.0 / D ** 0.5
-    q = synth.device_normal((N, Hq, D), 9, 1, dev, torch.bfloat16)
-    v = synth.device_normal((N, 1, D), 9, 3, dev, torch.bfloat16)
+    q = synth.device_normal((N, Hq, D), seed, 1, dev, torch.bfloat16)
+    v = synth.device_normal((N, 1, D), seed, 3, dev, torch.bfloat16)
     k = torch.zeros((N, 1, D), dtype=torch.bfloat16, device=dev)
-    rows = sorted({0, 5, 1000, 32767, 32768, 40000, 65535, 65536, 100000, 131071, 262143, 262144, 300001,
-                   500000, 524288, 640000, 777777, 900000, 1000000, 1048575}
-                  | set(np.random.Generator(np.random.PCG64(9)).integers(0, N, 12).tolist()))
     R = torch.tensor(rows, device=dev)
     n_r = (R + 1).double()
     do = torch.zeros((N, Hq, D), dtype=torch.bfloat16, device=dev)
-    do[R] = (synth.device_normal((len(rows), Hq, D), 9, 4, dev, torch.float32) * (n_r / 16.0)[:, None, None].float()
+    do[R] = (synth.device_normal((len(rows), Hq, D), seed, 4, dev, torch.float32) * (n_r / 16.0)[:, None, None].float()
              ).to(torch.bfloat16)
     o, lse = ul.attn_fwd(q, k, v, None)
     dq, dk, dv = ul.attn_bwd(q, k, v, o, do, lse, None)
@@ -222,9 +215,32 @@ def test_million_zero_keys_closed_forms():
     if lo < N:
         dk_err = max(dk_err, float(dk[lo:].abs().max()))
         dv_err = max(dv_err, float(dv[lo:].abs().max()))
-    log(f"  million K=0: max|dK - closed form| {dk_err:.3e}, max|dV - closed form| {dv_err:.3e}, "
+    log(f"  K=0 N={N} Hq={Hq} D={D}: max|dK - closed form| {dk_err:.3e}, max|dV - closed form| {dv_err:.3e}, "
         f"max|dK| {float(dk.abs().max()):.3f}, max|dV| {float(dv.abs().max()):.3f}")
     assert dk_err <= TOL_OUT and dv_err <= TOL_OUT
+
+
+@pytest.mark.timeout(300)
+def test_million_zero_keys_closed_forms():
+    """The K = 0 closed forms over the million-token document (4 q / 1 KV heads,
+    D = 128): 32 rows of R spread over the sequence."""
+    require_gpu()
+    log("path million K=0, sparse dO")
+    rows = sorted({0, 5, 1000, 32767, 32768, 40000, 65535, 65536, 100000, 131071, 262143, 262144, 300001,
+                   500000, 524288, 640000, 777777, 900000, 1000000, 1048575}
+                  | set(np.random.Generator(np.random.PCG64(9)).integers(0, 1 << 20, 12).tolist()))
+    _zero_keys_closed_forms(1 << 20, 4, 128, rows, 9)
+
+
+@pytest.mark.timeout(300)
+def test_split_key_blocks_zero_keys_closed_forms():
+    """The K = 0 closed forms where a window of 2048 query tiles is only 8192
+    tokens (16 query heads on one KV head, D = 64): the 24576-token document
+    spans three windows, so its first 64 key blocks are split."""
+    require_gpu()
+    log("K=0 split key blocks, 16 q / 1 KV heads")
+    rows = [0, 3, 700, 4095, 8191, 8192, 9000, 12000, 16383, 16384, 17000, 20000, 24000, 24575]
+    _zero_keys_closed_forms(24576, 16, 64, rows, 12)
 
 
 @pytest.mark.timeout(300)
