@@ -113,7 +113,8 @@ ul_status ul_doc_bounds(const int32_t *position_ids, int32_t *doc_start, int32_t
  * UL_DOC_BOUNDS_NOALLOC_MAX_N.  The call allocates nothing.  Every call on
  * one GPU shares that GPU's array: calls that overlap in time on one GPU (on
  * different streams, or from different threads) race and must not be issued.
- * `stream` must belong to the current device.  Errors: as ul_doc_bounds, and
+ * The array used is that of the stream's device (the current device for the
+ * null stream); the pointers must be on that device.  Errors: as ul_doc_bounds, and
  * UL_ERR_ARG for N > UL_DOC_BOUNDS_NOALLOC_MAX_N; UL_ERR_HIP if the array's
  * device address cannot be obtained.
  */

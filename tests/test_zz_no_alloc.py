@@ -62,3 +62,20 @@ def test_no_alloc_refuses_sizes_beyond_its_array():
     N = (1 << 26) + 1
     assert lib.ul_doc_bounds_noalloc(None, 0x10000000, 0x40000000, N, None) == ul.UL_ERR_ARG
     assert "allocation-free" in lib.ul_last_error().decode()
+
+
+def test_no_alloc_on_a_created_stream():
+    """A stream other than the null stream: the array is that of the stream's device."""
+    require_gpu()
+    lib = ul.load()
+    N = 200_001
+    pos = torch.from_numpy(synth.random_positions(N, 13, max_docs=50)).to("cuda:0")
+    ref_s, ref_e = _with_workspace(lib, pos, N, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    ds = torch.empty(N, dtype=torch.int32, device="cuda:0")
+    de = torch.empty(N, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        _no_alloc(lib, pos, N, ds, de, ctypes.c_void_p(st.cuda_stream))
+    st.synchronize()
+    assert torch.equal(ds, ref_s) and torch.equal(de, ref_e)

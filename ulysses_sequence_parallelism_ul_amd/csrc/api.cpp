@@ -272,7 +272,7 @@ ul_status ul_doc_bounds_noalloc(const int32_t* position_ids, int32_t* doc_start,
   st = check_position_ids(position_ids, N, bufs, 2);
   if (st != UL_OK) return st;
   int32_t* scan = nullptr;
-  hipError_t e = ul::noalloc_scan_scratch(&scan);
+  hipError_t e = ul::noalloc_scan_scratch((hipStream_t)stream, &scan);
   if (e != hipSuccess) return hip_status(e, "scratch address lookup");
   return hip_status(ul::launch_doc_bounds(position_ids, doc_start, doc_end, scan, (int)N, (hipStream_t)stream),
                     "doc_bounds launch");

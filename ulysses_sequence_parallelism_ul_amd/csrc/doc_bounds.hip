@@ -132,15 +132,29 @@ int32_t* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per d
 // device, and only that address is ever passed to a kernel.
 static __device__ __align__(256) int32_t scratch[2 * ((kNoAllocMaxN + kScanBlock - 1) / kScanBlock)];
 
-hipError_t noalloc_scan_scratch(int32_t** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
+hipError_t noalloc_scan_scratch(hipStream_t stream, int32_t** out) {
+  // the device the work will run on: the stream's, or the current one for the null stream
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return e;
+    dev = (int)d;
+  }
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (g_scratch_ptr[dev] == nullptr) {
+    // once per device, with that device current
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
     void* ptr = nullptr;
     e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
     if (e != hipSuccess) return e;
     g_scratch_ptr[dev] = static_cast<int32_t*>(ptr);
   }

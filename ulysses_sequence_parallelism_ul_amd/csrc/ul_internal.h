@@ -82,9 +82,10 @@ hipError_t launch_relayout(const void* src, void* dst, int64_t N, int H, int D, 
                            int elem_bytes, bool seq_to_head, hipStream_t s);
 hipError_t launch_doc_bounds(const int32_t* pos, int32_t* doc_start, int32_t* doc_end,
                              int32_t* scan_scratch, int N, hipStream_t s);
-// Device address, on the current device, of the fixed scan-partials array of
-// the allocation-free document bounds (looked up once per device).
-hipError_t noalloc_scan_scratch(int32_t** out);
+// Device address, on the device of `stream` (the current device for the null
+// stream), of the fixed scan-partials array of the allocation-free document
+// bounds (looked up once per device).
+hipError_t noalloc_scan_scratch(hipStream_t stream, int32_t** out);
 // [cols][D] bf16 view (column c -> token c >> lgG, head (hk << lgG) + (c & (G-1)) of a
 // [N][H][D] tensor) -> blocked transpose [Hkv][ceil(ncols / kTB)][D][kTB], zero-padded.
 hipError_t launch_transpose_blocked(const bf16* src, bf16* dst, int64_t ncols, int H, int Hkv, int lgG, int D,
