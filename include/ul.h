@@ -237,10 +237,10 @@ ul_status ul_rank_attn_bwd(const void *q_seq, const void *k_seq, const void *v_s
  *   q_send [P][M][Hq/P][D] and k_send / v_send [P][M][Hkv/P][D], block j
  *   holding heads [j H/P, (j+1) H/P) for rank j (the exchange then delivers
  *   rank j the blocks j of every shard, i.e. ul_seq_to_head's x_head).
- *   hidden must be a multiple of 64; Hq and Hkv multiples of P.
+ *   hidden must be a multiple of 64 (at most 2^22); Hq and Hkv multiples of P.
  * ul_out_proj: o_seq [M][HqD] (the attention output back in the sequence
  *   layout, read as is) times w_o [hidden][HqD] -> y [M][hidden];
- *   HqD must be a multiple of 64.
+ *   HqD must be a multiple of 64 (at most 2^22).
  * Errors: UL_ERR_ARG for the shape rules, null or misaligned pointers, outputs
  * overlapping anything; UL_ERR_UNSUPPORTED for dt != UL_BF16.  No workspace.
  */

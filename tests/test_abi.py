@@ -176,12 +176,14 @@ def test_projection_rejections_cpu():
         return lib.ul_qkv_proj_pack(x, B, q, D_, E, M, hidden, Hq, Hkv, D, P, dt, None)
 
     assert qkv(hidden=100) == ul.UL_ERR_ARG
+    assert qkv(hidden=(1 << 22) + 64) == ul.UL_ERR_ARG   # above the 2^22 limit
     assert qkv(Hkv=3) == ul.UL_ERR_ARG      # not a multiple of P
     assert qkv(M=0) == ul.UL_ERR_ARG
     assert qkv(dt=ul.UL_F32) == ul.UL_ERR_UNSUPPORTED
     assert qkv(x=None) == ul.UL_ERR_ARG
     assert qkv(q=A) == ul.UL_ERR_ARG        # q_send overlaps x
     assert lib.ul_out_proj(A, B, C, 16, 64, 96, ul.UL_BF16, None) == ul.UL_ERR_ARG   # HqD % 64
+    assert lib.ul_out_proj(A, B, C, 16, 64, (1 << 22) + 64, ul.UL_BF16, None) == ul.UL_ERR_ARG  # above 2^22
     assert lib.ul_out_proj(A, B, A, 16, 64, 128, ul.UL_BF16, None) == ul.UL_ERR_ARG  # y overlaps o_seq
     assert lib.ul_out_proj(A, B, C, 16, 64, 128, ul.UL_F32, None) == ul.UL_ERR_UNSUPPORTED
 

@@ -38,6 +38,8 @@ QKV_CASES = [
     (256, 256, 8, 2, 128, 2),
     (300, 512, 8, 8, 64, 8),
     (513, 1024, 32, 8, 128, 8),
+    (600, 320, 6, 3, 40, 3),     # several row and column tiles, both ragged
+    (40, 128, 4, 2, 12, 2),      # D not a multiple of 8: element-wise stores
 ]
 
 
@@ -56,7 +58,8 @@ def test_qkv_proj_pack_small(M, hidden, Hq, Hkv, D, P):
         assert _bar_ok(np64(got), ref), name
 
 
-@pytest.mark.parametrize("M,hidden,HqD", [(1, 64, 64), (77, 200, 128), (256, 4096, 256), (700, 512, 4096)])
+@pytest.mark.parametrize("M,hidden,HqD", [(1, 64, 64), (77, 200, 128), (256, 4096, 256), (700, 512, 4096),
+                                          (50, 100, 64), (300, 1000, 256)])
 def test_out_proj_small(M, hidden, HqD):
     require_gpu()
     log(f"out_proj M={M} hidden={hidden} HqD={HqD}")

@@ -526,7 +526,8 @@ ul_status ul_qkv_proj_pack(const void* x, const void* w_qkv, void* q_send, void*
                            void* stream) {
   if (dt != UL_BF16) return fail(UL_ERR_UNSUPPORTED, "the projections take bf16 (dtype %d)", (int)dt);
   if (M < 1) return fail(UL_ERR_ARG, "M=%lld must be >= 1", (long long)M);
-  if (hidden < 64 || hidden % 64 != 0) return fail(UL_ERR_ARG, "hidden=%d must be a positive multiple of 64", hidden);
+  if (hidden < 64 || hidden % 64 != 0 || hidden > (1 << 22))
+    return fail(UL_ERR_ARG, "hidden=%d must be a positive multiple of 64, at most 2^22", hidden);
   if (D < 1 || P < 1 || Hq < 1 || Hkv < 1) return fail(UL_ERR_ARG, "D, P, Hq and Hkv must be >= 1");
   if (Hq % P != 0 || Hkv % P != 0)
     return fail(UL_ERR_ARG, "Hq=%d and Hkv=%d must be multiples of P=%d", Hq, Hkv, P);
@@ -555,7 +556,8 @@ ul_status ul_out_proj(const void* o_seq, const void* w_o, void* y, int64_t M, in
   if (dt != UL_BF16) return fail(UL_ERR_UNSUPPORTED, "the projections take bf16 (dtype %d)", (int)dt);
   if (M < 1) return fail(UL_ERR_ARG, "M=%lld must be >= 1", (long long)M);
   if (hidden < 1) return fail(UL_ERR_ARG, "hidden=%d must be >= 1", hidden);
-  if (HqD < 64 || HqD % 64 != 0) return fail(UL_ERR_ARG, "Hq*D=%d must be a positive multiple of 64", HqD);
+  if (HqD < 64 || HqD % 64 != 0 || HqD > (1 << 22))
+    return fail(UL_ERR_ARG, "Hq*D=%d must be a positive multiple of 64, at most 2^22", HqD);
   Buf bufs[3] = {{o_seq, (size_t)M * HqD * 2, "o_seq"}, {w_o, (size_t)hidden * HqD * 2, "w_o"},
                  {y, (size_t)M * hidden * 2, "y"}};
   for (int i = 0; i < 3; ++i) {

@@ -13,25 +13,27 @@
 //  * output projection: plain row-major y [M][Nc], reading the attention output
 //    in the sequence layout [M][Hq*D] that head->seq produced, as is.
 //
-// Tiling: 256 x 256 output tile per work-group of 8 waves (two per SIMD), each
-// wave 128 rows x 64 columns (4 x 2 blocks of v_mfma_f32_32x32x16_bf16), K in
-// stages of 64 double-buffered in LDS (rows of 128 bytes, 16-byte chunks XOR
-// swizzled by row so 32 rows read at one chunk hit distinct banks), the next
-// stage copied global -> LDS by DMA while the current one is multiplied.
-// Work-groups are mapped so each XCD runs groups of 8 row tiles x 4 column
-// tiles together, sharing every K stage's slices of A and B through its L2.
+// Tiling: 256 x 256 output tile per work-group of 4 waves (one per SIMD), each
+// wave 128 x 128 (8 x 8 blocks of v_mfma_f32_16x16x32_bf16), K in stages of 64
+// double-buffered in LDS (rows of 128 bytes, 16-byte chunks XOR-swizzled by
+// row), the next stage copied global -> LDS by DMA while the current one is
+// multiplied, the instruction order fixed slot by slot (below), and the output
+// staged through LDS so it leaves in 16-byte runs.  Work-groups are mapped so
+// each XCD runs groups of 8 row tiles x 4 column tiles together, sharing every
+// K stage's slices of A and B through its L2.  Under sustained load the board
+// holds its power cap, and the 16x16x32 MFMA shape let it keep a higher clock
+// than 32x32x16 for the same work (measured).
 #include "ul_internal.h"
 
 namespace ul {
 namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kRowBytes = kBK * 2;                  // 128 bytes per tile row
 constexpr int kTileBytes = kBM * kRowBytes;         // 32 KiB per operand tile
 constexpr int kStage = 2 * kTileBytes;              // A tile + B tile
-constexpr int kChunksPerTile = kTileBytes / 16;     // 2048
-constexpr int kLoadsPerThread = kChunksPerTile / kThreads;  // 4 per operand (16 bytes each)
+constexpr int kDma = kTileBytes / 16 / kThreads;    // 8 copies of 16 bytes per operand and thread
 constexpr int kXcds = 8;
 constexpr int kGR = 8, kGC = 4;  // tile group per XCD: 8 row tiles x 4 column tiles
 
@@ -44,10 +46,12 @@ struct ColPtr {
   int64_t stride;
 };
 
+// vec(Nc): runs of eight columns starting at a multiple of 8 are contiguous and 16-byte aligned.
 struct EpiRowMajor {
   bf16* y;
   int64_t ld;
   __device__ ColPtr col(int n) const { return ColPtr{y + n, ld}; }
+  __device__ bool vec(int Nc) const { return (Nc & 7) == 0 && (ld & 7) == 0; }
 };
 
 struct EpiPackQKV {
@@ -69,17 +73,15 @@ struct EpiPackQKV {
     // [j][m][hl][d]: row m of destination block j
     return ColPtr{base + ((int64_t)j * M * hr + hl) * D + d, (int64_t)hr * D};
   }
+  __device__ bool vec(int) const { return (D & 7) == 0; }
 };
 
 template <class Epi>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int64_t M, int Nc, int K,
                     int n_row_tiles, int n_col_tiles, Epi epi) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
-  // XCD-aware tile order: work-group b runs on XCD b % 8; the 32 consecutive
-  // work-groups of one XCD form a group of 8 row tiles x 4 column tiles, whose
-  // A and B slices of each K stage are shared through that XCD's L2.
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds, local = bid / kXcds;
   const int grp = (local / (kGR * kGC)) * kXcds + xcd, within = local % (kGR * kGC);
@@ -89,106 +91,149 @@ gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int6
   if (rt >= n_row_tiles || ct >= n_col_tiles) return;
   const int64_t m0 = (int64_t)rt * kBM;
   const int n0 = ct * kBN;
-  const int wm = w >> 2, wn = w & 3;  // wave grid 2 x 4: 128 rows x 64 columns each
+  const int wm = w >> 1, wn = w & 1;  // wave grid 2 x 2: 128 rows x 128 columns each
 
-  // Tiles go global -> LDS by DMA (global_load_lds_dwordx4): lane l of wave w's
-  // i-th load writes the 16 bytes at LDS block (w * 4 + i) * 1024 + l * 16 of
-  // the tile, so each lane fetches the global chunk that the XOR-swizzled
-  // layout puts there.  Issued as inline assembly so that the compiler does
-  // not order the MFMA phase's LDS reads (of the other stage) behind them; the
-  // wave waits for its own copies before each barrier.
-  const bf16* pa[kLoadsPerThread];
-  const bf16* pb[kLoadsPerThread];
+  // Copies go global -> LDS by DMA with a scalar base (the tile's first row, advanced by the K stage)
+  // and a per-lane 32-bit byte offset: lane l of wave w's i-th copy fetches the 16-byte chunk of
+  // tile row w * 64 + 8 i + l / 8 that the XOR-swizzled layout keeps at LDS block (w * kDma + i),
+  // byte 16 l.  Rows past the end of the matrix read its last row.
+  const bf16* a_tile = A + m0 * K;
+  const bf16* b_tile = B + (int64_t)n0 * K;
+  uint32_t oa[kDma], ob[kDma];
 #pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int row = (w * kLoadsPerThread + i) * 8 + (l >> 3);
+  for (int i = 0; i < kDma; ++i) {
+    const int row = (w * kDma + i) * 8 + (l >> 3);
     const int chunk = (l & 7) ^ (row & 7);
-    const int64_t am = min<int64_t>(m0 + row, M - 1);   // rows past the end read the last row
-    const int bn = min(n0 + row, Nc - 1);
-    pa[i] = A + am * K + chunk * 8;
-    pb[i] = B + (int64_t)bn * K + chunk * 8;
+    oa[i] = (uint32_t)((min<int64_t>(row, M - 1 - m0) * K + chunk * 8) * 2);
+    ob[i] = (uint32_t)(((int64_t)min(row, Nc - 1 - n0) * K + chunk * 8) * 2);
   }
   typedef __attribute__((address_space(3))) char lds_char;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
-  auto dma = [&](int kt, int st) {
-    const int k0 = kt * kBK;
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      const uint32_t ba = __builtin_amdgcn_readfirstlane(lds0 + st * kStage + (w * kLoadsPerThread + i) * 1024);
-      const uint32_t bb = ba + kTileBytes;
-      // one wait state between writing M0 and the LDS DMA that reads it
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(ba), "v"(pa[i] + k0)
-                   : "memory", "m0");
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(bb), "v"(pb[i] + k0)
-                   : "memory", "m0");
-    }
+  auto dma = [&](int kt, int st, int i) {
+    const uint32_t ba = __builtin_amdgcn_readfirstlane(lds0 + st * kStage + (w * kDma + i) * 1024);
+    const uint32_t bb = ba + kTileBytes;
+    const bf16* sa = a_tile + kt * kBK;
+    const bf16* sb = b_tile + kt * kBK;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(ba), "v"(oa[i]), "s"(sa)
+                 : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(bb), "v"(ob[i]), "s"(sb)
+                 : "memory", "m0");
   };
   auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-  f32x16 acc[4][2];
+  // v_mfma_f32_16x16x32_bf16: lane l holds row (column) l % 16 of a 16-row A (16-column B) block at
+  // K chunk 4 ks + l / 16 of the 64-deep stage; the accumulator holds column l % 16, rows 4 (l / 16) + 0..3.
+  const int r16 = l & 15, q = l >> 4;
+  auto offa = [&](int i, int ks) { return swz(wm * 128 + i * 16 + r16, ks * 4 + q); };
+  auto offb = [&](int j, int ks) { return kTileBytes + swz(wn * 128 + j * 16 + r16, ks * 4 + q); };
+
+  f32x4 acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+
+  bf16x8 fa0[8], fb0[8], fa1[8], fb1[8];
+  // one operand fragment: x < 8 is row block x of A, else column block x - 8 of B
+  auto rd1 = [&](const char* s, int ks, bf16x8* fa, bf16x8* fb, int x) {
+    if (x < 8)
+      fa[x] = *reinterpret_cast<const bf16x8*>(s + offa(x, ks));
+    else
+      fb[x - 8] = *reinterpret_cast<const bf16x8*>(s + offb(x - 8, ks));
+  };
+  auto mf = [&](const bf16x8* fa, const bf16x8* fb, int t) {
+    const int i = t >> 3, j = t & 7;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
 
   const int nk = K / kBK;
-  dma(0, 0);
-  dma_wait();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) dma(kt + 1, st ^ 1);  // the other stage is free since the last barrier
-    const char* sa = smem + st * kStage;
-    const char* sb = sa + kTileBytes;
+  // Issue order, slot by slot (one MFMA per slot): after the barrier, k-step 0's sixteen reads with the
+  // previous stage's last sixteen MFMAs; k-step 0's 64 MFMAs with k-step 1's reads in their first
+  // sixteen slots; the next stage's copies spread over the first 60 slots; k-step 1's first 48 MFMAs,
+  // then the barrier.  The last stage copies its own K range again into the idle buffer.
+  auto stage = [&](int kt, int st, bool first) {
+    const char* s = smem + st * kStage;
+    const int kn = min(kt + 1, nk - 1);
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 a[4], b[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + i * 32 + lc, ks * 2 + g));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(sb + swz(wn * 64 + j * 32 + lc, ks * 2 + g));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int t = 0; t < 16; ++t) {
+      rd1(s, 0, fa0, fb0, t);
+      if (!first) mf(fa1, fb1, 48 + t);
+      if (t == 4 || t == 12) dma(kn, st ^ 1, t == 4 ? 0 : 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // schedule: nine operand reads ahead, then groups of four MFMAs and three
-    // reads (each 16-deep step needs six reads for eight MFMAs)
-    __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    for (int t = 0; t < 64; ++t) {
+      mf(fa0, fb0, t);
+      if (t < 16) rd1(s, 1, fa1, fb1, t);
+      if (t % 8 == 4 && t < 48) dma(kn, st ^ 1, 2 + t / 8);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+#pragma unroll
+    for (int t = 0; t < 48; ++t) {
+      mf(fa1, fb1, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     dma_wait();
     __syncthreads();
-  }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // C block (i, j): lane holds rows (e>>2)*8 + g*4 + (e&3) of column lc
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kDma; ++i) dma(0, 0, i);
+  dma_wait();
+  __syncthreads();
+  stage(0, 0, true);
+  int kt = 1;
+  for (; kt + 1 < nk; kt += 2) {
+    stage(kt, 1, false);
+    stage(kt + 1, 0, false);
+  }
+  if (kt < nk) stage(kt, 1, false);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + lc;
-      if (n >= Nc) continue;
-      const ColPtr cp = epi.col(n);
+  for (int t = 48; t < 64; ++t) mf(fa1, fb1, t);
+
+  // Epilogue through LDS (free since the last barrier): each wave stages its 128 x 128 block as bf16
+  // rows of 256 bytes, 16-byte chunks XOR-swizzled by row, and writes it back in runs of eight
+  // columns (16 bytes), four rows of 256 bytes per store instruction.
+  char* ws = smem + w * 32768;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 128 + i * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-        if (m < M) cp.p[m * cp.stride] = (bf16)acc[i][j][e];
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = i * 16 + q * 4 + e, c = j * 16 + r16;
+        *reinterpret_cast<bf16*>(ws + r * 256 + ((((c >> 3) ^ (r & 15))) << 4) + (c & 7) * 2) = (bf16)acc[i][j][e];
       }
+  const bool vec = epi.vec(Nc);
+#pragma unroll 4
+  for (int qq = 0; qq < 32; ++qq) {
+    const int x = qq * 64 + l, r = x >> 4, cc = x & 15;
+    const bf16x8 val = *reinterpret_cast<const bf16x8*>(ws + r * 256 + ((cc ^ (r & 15)) << 4));
+    const int64_t m = m0 + wm * 128 + r;
+    const int n = n0 + wn * 128 + cc * 8;
+    if (m >= M || n >= Nc) continue;
+    if (vec) {
+      const ColPtr cp = epi.col(n);
+      *reinterpret_cast<bf16x8*>(cp.p + m * cp.stride) = val;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (n + t < Nc) {
+          const ColPtr cp = epi.col(n + t);
+          cp.p[m * cp.stride] = val[t];
+        }
     }
+  }
 }
 
 template <class Epi>
 hipError_t launch_gemm(const bf16* A, const bf16* B, int64_t M, int Nc, int K, const Epi& epi, const char* name,
                        hipStream_t s) {
-  if (M < 1 || Nc < 1 || K < kBK || K % kBK != 0) return hipErrorInvalidValue;
+  // K <= 2^22 keeps the copies' per-lane byte offsets (up to 255 rows of K) within 32 bits
+  if (M < 1 || Nc < 1 || K < kBK || K % kBK != 0 || K > (1 << 22)) return hipErrorInvalidValue;
   const int64_t nrt = (M + kBM - 1) / kBM;
   const int nct = (Nc + kBN - 1) / kBN;
   const int64_t ngroups = ((nrt + kGR - 1) / kGR) * ((nct + kGC - 1) / kGC);
