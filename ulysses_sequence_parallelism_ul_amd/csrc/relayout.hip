@@ -14,10 +14,7 @@
 namespace ul {
 namespace {
 
-constexpr int kThreads = 512;  // measured best of {256, 512} x unroll {1, 2, 4} at N = 1M
-constexpr int kUnroll = 1;
-
-template <typename T>
+template <typename T, int kThreads, int kUnroll>
 __global__ void __launch_bounds__(kThreads) relayout_kernel(const T* __restrict__ src, T* __restrict__ dst,
                                                           int64_t total, int64_t run, int lg_run,
                                                           int64_t stride, int64_t off, int seq_to_head) {
@@ -63,19 +60,33 @@ int ilog2_exact(int64_t x) {
   return l;
 }
 
-template <typename T>
-hipError_t launch_t(const void* src, void* dst, int64_t N, int64_t run_bytes, int64_t row_bytes,
-                    int64_t off_bytes, bool s2h, hipStream_t s) {
+template <typename T, int kThreads, int kUnroll>
+hipError_t launch_shape(const void* src, void* dst, int64_t N, int64_t run_bytes, int64_t row_bytes,
+                        int64_t off_bytes, bool s2h, hipStream_t s) {
   const int64_t run = run_bytes / (int64_t)sizeof(T);
   const int64_t total = N * run;
   const int64_t per_block = (int64_t)kThreads * kUnroll;
   const int64_t blocks = (total + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   TimedLaunch timer(s2h ? "relayout_seq_to_head" : "relayout_head_to_seq", s);
-  hipLaunchKernelGGL(relayout_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((relayout_kernel<T, kThreads, kUnroll>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
                      static_cast<const T*>(src), static_cast<T*>(dst), total, run, ilog2_exact(run),
                      row_bytes / (int64_t)sizeof(T), off_bytes / (int64_t)sizeof(T), s2h ? 1 : 0);
   return hipGetLastError();
+}
+
+// Block size and units per thread by run length and direction, the fastest of {256, 512, 1024}
+// threads x {1, 2} units measured per shape at the million-token share (256 B - 2 KiB runs, both
+// directions): short runs favour small blocks, 2 KiB runs large ones, and the 512 B head->seq
+// writes two units per thread.
+template <typename T>
+hipError_t launch_t(const void* src, void* dst, int64_t N, int64_t run_bytes, int64_t row_bytes,
+                    int64_t off_bytes, bool s2h, hipStream_t s) {
+  if (run_bytes >= 2048) return launch_shape<T, 1024, 1>(src, dst, N, run_bytes, row_bytes, off_bytes, s2h, s);
+  if (run_bytes <= 256 || (s2h && run_bytes > 512))
+    return launch_shape<T, 256, 1>(src, dst, N, run_bytes, row_bytes, off_bytes, s2h, s);
+  if (!s2h && run_bytes <= 512) return launch_shape<T, 512, 2>(src, dst, N, run_bytes, row_bytes, off_bytes, s2h, s);
+  return launch_shape<T, 512, 1>(src, dst, N, run_bytes, row_bytes, off_bytes, s2h, s);
 }
 
 }  // namespace
