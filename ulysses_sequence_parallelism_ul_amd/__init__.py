@@ -52,7 +52,8 @@ UL_OK, UL_ERR_ARG, UL_ERR_UNSUPPORTED, UL_ERR_HIP = 0, 1, 2, 3
 UL_F32, UL_BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libul.so")
+# UL_LIBRARY_PATH selects another build of the same library (e.g. the host-ASan one)
+library_path = os.environ.get("UL_LIBRARY_PATH") or os.path.join(_HERE, "libul.so")
 _lib = None
 
 _P = ctypes.c_void_p

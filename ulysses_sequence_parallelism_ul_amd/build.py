@@ -70,5 +70,47 @@ def build(verbose=False, jobs=None):
     return LIB_PATH
 
 
+# Host-side AddressSanitizer for the C ABI layer (argument validation, error
+# strings, workspace arithmetic): the .cpp sources are compiled again with ASan
+# and linked with the already-built kernel objects into a separate library.
+# Device code is not instrumented (GPU ASan is not used here).
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libul_asan.so")
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime():
+    """Path of the ASan runtime that a process loading ASAN_LIB must preload, or None."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    return path if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path) else None
+
+
+def build_host_asan(verbose=False):
+    """Build ASAN_LIB from csrc/*.cpp (ASan) plus the kernel objects of the last build()."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    cpps = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".cpp"))
+    kern = sorted(os.path.join(BUILD_DIR, f) for f in os.listdir(BUILD_DIR) if f.endswith(".hip.o"))
+    if not kern:
+        raise RuntimeError("no kernel objects in _build/; run build() first")
+    objs = []
+    for src in cpps:
+        obj = os.path.join(ASAN_DIR, os.path.basename(src) + ".o")
+        flags = [f for f in HIPCC_FLAGS if not f.startswith("--offload-arch")]
+        cmd = [_hipcc()] + flags + ASAN_HOST_FLAGS + ["-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+        objs.append(obj)
+    cmd = ([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+            "-shared-libsan", "-o", ASAN_LIB] + kern + objs)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose="-v" in sys.argv)
