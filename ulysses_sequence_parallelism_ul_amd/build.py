@@ -17,6 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libul.so")
+PROBE_SRC = os.path.join(HERE, "probe", "mfma_rate.hip")
+PROBE_LIB = os.path.join(HERE, "libul_probe.so")  # calibration probe (bench.py --mfma-ceiling), not the ABI
 
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled for every HIP translation unit.
@@ -67,7 +69,21 @@ def build(verbose=False, jobs=None):
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")
+    build_probe(verbose)
     return LIB_PATH
+
+
+def build_probe(verbose=False):
+    """Compile the MFMA-rate calibration probe into its own library, PROBE_LIB."""
+    obj = os.path.join(BUILD_DIR, "probe_mfma_rate.o")
+    _compile(PROBE_SRC, obj, verbose)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 # Host-side AddressSanitizer for the C ABI layer (argument validation, error
@@ -90,7 +106,7 @@ def build_host_asan(verbose=False):
     """Build ASAN_LIB from csrc/*.cpp (ASan) plus the kernel objects of the last build()."""
     os.makedirs(ASAN_DIR, exist_ok=True)
     cpps = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".cpp"))
-    kern = sorted(os.path.join(BUILD_DIR, f) for f in os.listdir(BUILD_DIR) if f.endswith(".hip.o"))
+    kern = sorted(os.path.join(BUILD_DIR, f) for f in os.listdir(BUILD_DIR) if f.endswith(".hip.o"))  # not the probe
     if not kern:
         raise RuntimeError("no kernel objects in _build/; run build() first")
     objs = []
