@@ -82,6 +82,9 @@ gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int6
                     int n_row_tiles, int n_col_tiles, Epi epi) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  // XCD-aware tile order: work-group b runs on XCD b % 8; the 32 consecutive
+  // work-groups of one XCD form a group of 8 row tiles x 4 column tiles, whose
+  // A and B slices of each K stage are shared through that XCD's L2.
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds, local = bid / kXcds;
   const int grp = (local / (kGR * kGC)) * kXcds + xcd, within = local % (kGR * kGC);
@@ -114,6 +117,8 @@ gemm_nt_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int6
     const uint32_t bb = ba + kTileBytes;
     const bf16* sa = a_tile + kt * kBK;
     const bf16* sb = b_tile + kt * kBK;
+    // one wait state between writing M0 and the LDS DMA that reads it; issued as inline assembly
+    // so that the compiler does not order LDS reads of the other stage behind the copies
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(ba), "v"(oa[i]), "s"(sa)
                  : "memory", "m0");
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(bb), "v"(ob[i]), "s"(sb)
