@@ -133,3 +133,78 @@ def test_rank_calls_graph_replays_match_eager():
                 a, b = a[:, cols], b[:, cols]
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager step"
         log(f"replay {rep} bit-identical")
+
+
+@pytest.mark.gpu
+def test_projection_and_loss_calls_graph_replays_match_eager():
+    """The projections and the loss entry points captured together (shard projection into the send blocks,
+    output projection, label shift, per-shard counts, their combination, cross entropy with its gradient on
+    two shards, and the combination of the loss sums): every replay equals the eager calls."""
+    require_gpu()
+    dev = torch.device("cuda:0")
+    M, hidden, Hq, Hkv, D, P, V = 1000, 512, 8, 2, 64, 2, 1000
+    log(f"graph capture of projections and loss M={M} hidden={hidden} V={V}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(79)
+
+    def rnd(*shape, s=1.0):
+        return (torch.randn(*shape, generator=g, device=dev) * s).to(torch.bfloat16)
+
+    x, o_in = rnd(M, hidden), rnd(M, Hq * D)
+    wqkv, wo = rnd((Hq + 2 * Hkv) * D, hidden, s=hidden ** -0.5), rnd(hidden, Hq * D, s=(Hq * D) ** -0.5)
+    labels = torch.randint(0, V, (M,), generator=g, device=dev, dtype=torch.int32)
+    labels[::7] = ul.IGNORE_INDEX
+    pos = torch.from_numpy(synth.position_ids_from_lengths([400, 1, 599])).to(dev)
+    T = M // P
+    logits = [rnd(T, V, s=2.0) for _ in range(P)]
+    q_send = torch.empty(P, M, Hq // P, D, dtype=torch.bfloat16, device=dev)
+    k_send = torch.empty(P, M, Hkv // P, D, dtype=torch.bfloat16, device=dev)
+    v_send = torch.empty_like(k_send)
+    y = torch.empty(M, hidden, dtype=torch.bfloat16, device=dev)
+    y_lab = torch.empty(M, dtype=torch.int32, device=dev)
+    counts = torch.empty(P, dtype=torch.int64, device=dev)
+    total = torch.empty(1, dtype=torch.int64, device=dev)
+    sums = torch.empty(P, dtype=torch.float64, device=dev)
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    loss_tok = torch.empty(M, dtype=torch.float32, device=dev)
+    dlogits = [torch.empty(T, V, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    outs = [q_send, k_send, v_send, y, y_lab, counts, total, sums, loss, loss_tok] + dlogits
+
+    def step():
+        ul.qkv_proj_pack(x, wqkv, Hq, Hkv, D, P, q_send, k_send, v_send)
+        ul.out_proj(o_in, wo, y)
+        ul.shift_labels(labels, pos, out=y_lab)
+        for r in range(P):
+            ul.ce_count(y_lab[r * T:(r + 1) * T], count=counts[r:r + 1])
+        ul.loss_combine(counts, total_count=total)
+        for r in range(P):
+            ul.cross_entropy(logits[r], y_lab[r * T:(r + 1) * T], total_count=total, grad=True,
+                             loss_tok=loss_tok[r * T:(r + 1) * T], loss_sum=sums[r:r + 1], dlogits=dlogits[r])
+        ul.loss_combine(counts, loss_sums=sums, total_count=total, loss=loss)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    assert int(total.item()) == int((y_lab != ul.IGNORE_INDEX).sum().item())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for rep in range(3):
+        for t in outs:
+            if t.is_floating_point():
+                t.fill_(float("nan"))
+            else:
+                t.fill_(-7)
+        gr.replay()
+        scratch = torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager calls"
+        log(f"replay {rep} bit-identical")
