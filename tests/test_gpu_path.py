@@ -7,6 +7,7 @@ independent library routine) and on sampled rows against the oracle; forward
 and dQ on sampled rows against the oracle; dK/dV on the last 64 keys of each
 of the first three documents against the oracle; per-document dK/dV sums; the
 Q = 0 and K = 0 closed forms at N = 1M (the latter on whole dK / dV tensors);
+a ragged N = 1,000,008 packed case on the last rank;
 determinism; and, for the training share, every
 document's O, LSE, dQ, dK and dV on whole tensors against the oracle run per
 document.
@@ -250,3 +251,61 @@ def test_training_share_deterministic():
     b = _run("train_packed")
     for name in ("o", "lse", "dq", "dk", "dv", "o_seq", "dq_seq"):
         assert torch.equal(a[name], b[name]), name
+
+
+@pytest.mark.timeout(400)
+def test_ragged_million_packed_last_rank():
+    """N = 1,000,008 (a multiple of the 8 ranks but of no tile size: 8 tokens past the last full 64-token tile),
+    three documents of 300,001, 7 and 700,000 tokens (the long ones split into query-tile windows, the short one
+    inside one key block), rank 7 of 8: exchanges bit-exact on whole tensors, forward and dQ on sampled rows
+    (the ragged tail included), dK/dV on the last 64 keys of every document, against the oracle."""
+    require_gpu()
+    N, HqA, HkvA, D, rank = 1_000_008, 32, 8, 128, 7
+    lengths = [300_001, 7, 700_000]
+    assert sum(lengths) == N and N % P == 0
+    log(f"ragged path N={N} docs={lengths} rank={rank}")
+    dev = torch.device("cuda:0")
+    seed = 41
+    q_seq = synth.device_normal((N, HqA, D), seed, 1, dev, torch.bfloat16)
+    k_seq = synth.device_normal((N, HkvA, D), seed, 2, dev, torch.bfloat16)
+    v_seq = synth.device_normal((N, HkvA, D), seed, 3, dev, torch.bfloat16)
+    do_seq = synth.device_normal((N, HqA, D), seed, 4, dev, torch.bfloat16)
+    pos_np = synth.position_ids_from_lengths(lengths)
+    pos = torch.from_numpy(pos_np).to(dev)
+    q, k, v, do = (ul.seq_to_head(x, P, rank) for x in (q_seq, k_seq, v_seq, do_seq))
+    o, lse = ul.attn_fwd(q, k, v, pos)
+    dq, dk, dv = ul.attn_bwd(q, k, v, o, do, lse, pos)
+    outs = {}
+    for name, t, hp in (("o", o, HqA // P), ("dq", dq, HqA // P), ("dk", dk, HkvA // P), ("dv", dv, HkvA // P)):
+        full = torch.zeros((N, hp * P, D), dtype=t.dtype, device=dev)
+        ul.head_to_seq(t, full, P, rank)
+        outs[name] = (full, hp)
+    torch.cuda.synchronize()
+    log("ragged path: exchanges")
+    for full, part, hp in ((q_seq, q, HqA // P), (k_seq, k, HkvA // P), (v_seq, v, HkvA // P), (do_seq, do, HqA // P)):
+        assert torch.equal(part.view(torch.int16), full[:, rank * hp:(rank + 1) * hp].contiguous().view(torch.int16))
+    for name, part in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        full, hp = outs[name]
+        assert torch.equal(full[:, rank * hp:(rank + 1) * hp], part)
+        assert torch.count_nonzero(full[:, :rank * hp]) == 0
+    del outs, q_seq, k_seq, v_seq, do_seq
+    log("ragged path: oracle forward and dQ rows")
+    qf, k64, v64, dof = (q.float().cpu().numpy(), k.double().cpu().numpy(), v.double().cpu().numpy(),
+                         do.float().cpu().numpy())
+    rng = np.random.Generator(np.random.PCG64(41))
+    starts = np.cumsum([0] + lengths[:-1])
+    edges = [b + d for b in list(starts) + [N - 8, N // 2, 65536] for d in (-1, 0, 1) if 0 <= b + d < N]
+    rows = np.unique(np.r_[0:32, N - 72:N, edges, rng.integers(0, N, 64)])
+    rr, eo, el = oracle.attn_fwd_rows(qf, k64, v64, pos_np, rows)
+    ri = torch.from_numpy(rr).to(dev)
+    assert max_abs(np64(o[ri]), eo) <= TOL_OUT
+    assert max_abs(np64(lse[:, ri]), el) <= TOL_LSE
+    rr, edq, _ = oracle.attn_bwd_dq_rows(qf, k64, v64, dof, pos_np, rows)
+    assert max_abs(np64(dq[torch.from_numpy(rr).to(dev)]), edq) <= TOL_OUT
+    log("ragged path: oracle dK/dV on the last keys of every document")
+    ends = starts + np.array(lengths) - 1
+    kv_rows = np.unique(np.concatenate([np.arange(max(s, e - 63), e + 1) for s, e in zip(starts, ends)]))
+    rr, edk, edv = oracle.attn_bwd_dkdv_rows(qf, k64, v64, dof, pos_np, kv_rows)
+    ri = torch.from_numpy(rr).to(dev)
+    assert max_abs(np64(dk[ri]), edk) <= TOL_OUT
+    assert max_abs(np64(dv[ri]), edv) <= TOL_OUT
