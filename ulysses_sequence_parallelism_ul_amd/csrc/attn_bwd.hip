@@ -24,9 +24,10 @@
 //    are read from the same tiles with the gfx950 LDS transpose read
 //    (ds_read_b64_tr_b16), so only 32 KiB per 64-column tile crosses from L2;
 //    those tiles are copied global -> LDS by DMA.
-//  * dq_kernel (query-outer, like the forward): a wave owns 32 query columns
-//    with Q and dO in registers; S^T and dP^T are recomputed per key tile and
-//    dQ^T += K^T dS^T takes K^T from the K tile by transpose reads.
+//  * dq_kernel_1w (D = 128) and dq_kernel (D = 64), query-outer like the
+//    forward: a wave owns 64 (dq_kernel_1w, one wave per SIMD) or 32 query
+//    columns with Q and dO in registers; S^T and dP^T are recomputed per key
+//    tile and dQ^T += K^T dS^T takes K^T from the K tile by transpose reads.
 // Tiles outside the causal band and outside the documents are never visited;
 // tiles that are fully visible skip the per-element mask.
 #include "ul_internal.h"
@@ -502,7 +503,6 @@ __global__ void __launch_bounds__(NW * 64) dq_kernel(
     int Hkv, int lgG, float sl2, float scale) {
   using C = DqCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
-  UL_CODE_PAD(11);  // tile loop at 24 bytes into a 64-byte line (D = 128)
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
   const int G = 1 << lgG;
   const int hk = blockIdx.x % Hkv;
@@ -629,6 +629,401 @@ __global__ void __launch_bounds__(NW * 64) dq_kernel(
   }
 }
 
+// ------------------------------------------------------ dQ, one wave per SIMD --
+// The same product as dq_kernel, for D = 128, with one wave per SIMD (512
+// registers per lane).  A wave owns 64 query columns (two 32-column blocks), so
+// every K, V and K^T fragment read from LDS feeds two MFMAs: half the LDS
+// operand bytes per MFMA of dq_kernel, which is what bounds these kernels.  Q
+// and dO (the B operands) and the dQ^T accumulators live in AGPRs for the whole
+// key loop; the MFMAs are inline assembly so that the compiler keeps them
+// there.  Each 32-key half-tile runs as S^T/dP^T MFMAs, then its softmax VALU
+// work interleaved with the next half's S^T/dP^T MFMAs, then its dQ MFMAs.
+// K/V tiles go global -> LDS by DMA into a ring of four stages, each copy two
+// tiles ahead (a tile's K^T is still read for its second half's dQ after the
+// next tile's first half).
+//
+// The compiler does not know that the asm statements are MFMAs, so it neither
+// inserts the wait states the hardware needs around them nor keeps their
+// operands from being reused too early.  The kernel supplies both:
+//  * s_nop fences, with the registers as "+" operands, between an MFMA and the
+//    first non-MFMA read of its result (q1_fence4, q1_fence_acc), and between a
+//    VALU write and an MFMA reading it (q1_fence_pk);
+//  * empty asm statements that use an MFMA's A operand in the slots after it,
+//    so nothing is placed in its registers while the MFMA still reads them;
+//  * no register copies into an accumulator: the first dQ MFMAs of a column
+//    block start from C = 0 instead of a zero fill, and Q / dO are loaded
+//    straight into AGPRs.
+// A compile-time test scans the kernel's machine code for the two hazards.
+template <int D>
+struct Dq1wCfg {
+  static constexpr int kThreads = 256;
+  static constexpr int BN = 64;
+  static constexpr int BMC = 256;
+  static constexpr int RSTR = D * 2;
+  static constexpr int RBYTES = BN * RSTR;
+  static constexpr int K_OFF = 0, V_OFF = RBYTES;
+  static constexpr int STAGE = 2 * RBYTES;
+  static constexpr int NS = 4;
+  static constexpr int RPT = BN * D / 8 / kThreads;
+  static_assert(RPT * kThreads * 8 == BN * D, "tile copies must split evenly");
+};
+
+__device__ __forceinline__ const bf16* uniform_ptr(const bf16* p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x), hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return reinterpret_cast<const bf16*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ void q1_mfma_v0(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void q1_mfma_v(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void q1_mfma_a0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void q1_mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// wait states after the last MFMA writing these (the compiler does not see the MFMAs)
+__device__ __forceinline__ void q1_fence4(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void q1_fence_pk(bf16x8 (&p)[2][2]) {
+  asm volatile("s_nop 4" : "+v"(p[0][0]), "+v"(p[0][1]), "+v"(p[1][0]), "+v"(p[1][1]));
+}
+template <int NB>
+__device__ __forceinline__ void q1_fence_acc(f32x16 (&acc)[2][NB]) {
+  if constexpr (NB == 4)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2"
+                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+                   "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]));
+}
+// keeps a register value live at this point
+__device__ __forceinline__ void q1_keep(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+// four 16-byte fragments straight into AGPRs (waits in the same block)
+__device__ __forceinline__ void q1_load4(bf16x8& r0, bf16x8& r1, bf16x8& r2, bf16x8& r3, const bf16* p, int stride) {
+  asm volatile(
+      "global_load_dwordx4 %0, %4, off\n\tglobal_load_dwordx4 %1, %5, off\n\t"
+      "global_load_dwordx4 %2, %6, off\n\tglobal_load_dwordx4 %3, %7, off\n\ts_waitcnt vmcnt(0)"
+      : "=&a"(r0), "=&a"(r1), "=&a"(r2), "=&a"(r3)
+      : "v"(p), "v"(p + stride), "v"(p + 2 * stride), "v"(p + 3 * stride)
+      : "memory");
+}
+
+template <int B, int E, class F>
+__device__ __forceinline__ void q1_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    q1_for<B + 1, E>(f);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) dq_kernel_1w(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ doc_start, const int32_t* __restrict__ order, float* __restrict__ dq, int N,
+    int Hkv, int lgG, float sl2, float scale) {
+  using C = Dq1wCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::NS * C::STAGE];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
+  const int G = 1 << lgG;
+  const int hk = blockIdx.x % Hkv;
+  const int cb = order[blockIdx.x / Hkv];
+  const int64_t NG = (int64_t)N << lgG;
+  const int64_t c0 = (int64_t)cb * C::BMC;
+  const int r_first = (int)(c0 >> lgG);
+  const int r_last = (int)min<int64_t>(N - 1, (c0 + C::BMC - 1) >> lgG);
+  const int t_lo = doc_start[r_first] / C::BN;
+  const int t_hi = r_last / C::BN;
+  const int ds_last = doc_start[r_last];
+
+  int row[2], ds_c[2];
+  bool cvalid[2];
+  int64_t qoff[2];
+  float lse2[2], dl[2];
+  bf16x8 qreg[2][D / 16], doreg[2][D / 16];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t c = c0 + w * 64 + j * 32 + lc;
+    cvalid[j] = c < NG;
+    row[j] = cvalid[j] ? (int)(c >> lgG) : -1;
+    ds_c[j] = cvalid[j] ? doc_start[row[j]] : 0;
+    qoff[j] = cvalid[j] ? col_offset(c, lgG, Hkv, hk, D) : 0;  // a column past the end reads column 0
+    lse2[j] = 0.0f;
+    dl[j] = 0.0f;
+    if (cvalid[j]) {
+      const int h = (hk << lgG) + (int)(c & (G - 1));
+      lse2[j] = lse[(int64_t)h * N + row[j]] * kLog2e;
+      dl[j] = delta[(int64_t)hk * NG + c];
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ks += 4) {
+      q1_load4(qreg[j][ks], qreg[j][ks + 1], qreg[j][ks + 2], qreg[j][ks + 3], q + qoff[j] + ks * 16 + g * 8, 16);
+      q1_load4(doreg[j][ks], doreg[j][ks + 1], doreg[j][ks + 2], doreg[j][ks + 3], dout + qoff[j] + ks * 16 + g * 8,
+               16);
+    }
+  }
+  f32x16 acc[2][D / 32];  // set by the first tile's first dQ MFMAs (no zero fill to copy between registers)
+
+  // DMA of a K / V tile: lane l of wave w's i-th copy fills byte (w * RPT + i) * 1024 + 16 l of the tile,
+  // the row and chunk the permuted, swizzled layout keeps there; keys past the end read the last key
+  int kr[C::RPT];
+  uint32_t kco[C::RPT];
+#pragma unroll
+  for (int i = 0; i < C::RPT; ++i) {
+    const int pb = (w * C::RPT + i) * 1024 + l * 16;
+    const int prow = pb / (D * 2), slot = (pb % (D * 2)) >> 4;
+    constexpr int CPR = D / 8;
+    kco[i] = (uint32_t)((slot ^ ((((prow & 3) << 2) ^ ((prow >> 2) & 3)) & (CPR - 1))) * 16);
+    kr[i] = tile_row(prow);
+  }
+  const uint32_t kstride = (uint32_t)(Hkv * D * 2);
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  auto dma = [&](int t, int st) __attribute__((always_inline)) {
+    const int t0 = t * C::BN;
+    const int lim = N - 1 - t0;
+    const bf16* kbase = uniform_ptr(k + ((int64_t)t0 * Hkv + hk) * D);
+    const bf16* vbase = uniform_ptr(v + ((int64_t)t0 * Hkv + hk) * D);
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) {
+      const uint32_t off = (uint32_t)min(kr[i], lim) * kstride + kco[i];
+      const uint32_t mk = __builtin_amdgcn_readfirstlane(lds0 + st * C::STAGE + C::K_OFF + (w * C::RPT + i) * 1024);
+      const uint32_t mv = mk + (C::V_OFF - C::K_OFF);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(mk), "v"(off), "s"(kbase)
+                   : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(mv), "v"(off), "s"(vbase)
+                   : "memory", "m0");
+    }
+  };
+  auto dma_wait = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // all but the last tile's copies (2 * RPT per thread) done
+  auto dma_wait_prev = [&]() __attribute__((always_inline)) {
+    static_assert(2 * C::RPT == 8, "copies per tile and thread");
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  };
+
+  // half-tile buffers: A for first halves (keys 0-31 of a tile), B for second halves
+  f32x16 sA[2], dpA[2], sB[2], dpB[2];
+  bf16x8 pkA[2][2], pkB[2][2];
+
+  // softmax work of one half-tile in 30 steps: per column block eight steps of two exponentials, the
+  // mask, four steps of dS, two of packing
+  struct Half {
+    f32x16* s;
+    f32x16* dp;
+    bf16x8 (*pk)[2];
+    int t, kb;
+    bool msk;
+  };
+  auto vstep = [&](auto k_c, const Half& h) __attribute__((always_inline)) {
+    constexpr int kk = decltype(k_c)::value;
+    constexpr int j = kk / 15, st = kk % 15;
+    f32x16& sj = h.s[j];
+    if constexpr (st < 8) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = st * 2 + e;
+        sj[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sj[i], sl2, -lse2[j]));
+      }
+    } else if constexpr (st == 8) {
+      if (h.msk) {
+        const int t0 = h.t * C::BN;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kv = t0 + h.kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+          sj[i] = (kv <= row[j] && kv >= ds_c[j]) ? sj[i] : 0.0f;
+        }
+      }
+    } else if constexpr (st < 13) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = (st - 9) * 4 + e;
+        sj[i] *= h.dp[j][i] - dl[j];
+      }
+    } else {
+      h.pk[j][st - 13] = pack8(sj, (st - 13) * 8);
+    }
+  };
+  constexpr int NVSTEP = 30;
+  auto pin = [&](const Half& h) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(h.s[0]), "+v"(h.s[1]), "+v"(h.pk[0][0]), "+v"(h.pk[0][1]), "+v"(h.pk[1][0]),
+                 "+v"(h.pk[1][1]));
+  };
+
+  // operand ring of the S/dP phases: K and V fragments two ks steps ahead; a phase's first two are
+  // read during the phase before it where that phase allows
+  bf16x8 ak[3], av[3];
+  auto rd = [&](const char* sb, int kb, int ks, int x) __attribute__((always_inline)) {
+    ak[x] = *reinterpret_cast<const bf16x8*>(sb + C::K_OFF + lds_off<D>(kb * 32 + lc, ks * 2 + g));
+    av[x] = *reinterpret_cast<const bf16x8*>(sb + C::V_OFF + lds_off<D>(kb * 32 + lc, ks * 2 + g));
+  };
+  // S^T and dP^T of half kb of the tile in stage `sb` into (s, dp), with softmax steps [VLO, VHI) of
+  // half-tile h between the MFMAs
+  auto sdp = [&](const char* sb, auto kb_c, f32x16 (&s)[2], f32x16 (&dp)[2], auto vlo_c, auto vhi_c, const Half& h,
+                 bool pre) __attribute__((always_inline)) {
+    constexpr int kb = decltype(kb_c)::value;
+    constexpr int VLO = decltype(vlo_c)::value, VHI = decltype(vhi_c)::value;
+    if (!pre) {
+      rd(sb, kb, 0, 0);
+      rd(sb, kb, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NSLOT = 4 * (D / 16);
+    q1_for<0, NSLOT>([&](auto m_c) __attribute__((always_inline)) {
+      constexpr int m = decltype(m_c)::value, ks = m / 4, sub = m % 4;
+      if constexpr (sub == 2 && ks + 2 < D / 16) {
+        // the fragments replaced here were last MFMA sources two or more slots ago; keeping them live
+        // until the load stops the compiler from putting temporaries there in between
+        asm volatile("" ::"v"(ak[(ks + 2) % 3]), "v"(av[(ks + 2) % 3]));
+        rd(sb, kb, ks + 2, (ks + 2) % 3);
+      }
+      if constexpr (sub == 0) {
+        if constexpr (ks == 0) q1_mfma_v0(s[0], ak[0], qreg[0][0]); else q1_mfma_v(s[0], ak[ks % 3], qreg[0][ks]);
+      } else if constexpr (sub == 1) {
+        if constexpr (ks == 0) q1_mfma_v0(s[1], ak[0], qreg[1][0]); else q1_mfma_v(s[1], ak[ks % 3], qreg[1][ks]);
+      } else if constexpr (sub == 2) {
+        if constexpr (ks == 0) q1_mfma_v0(dp[0], av[0], doreg[0][0]); else q1_mfma_v(dp[0], av[ks % 3], doreg[0][ks]);
+      } else {
+        if constexpr (ks == 0) q1_mfma_v0(dp[1], av[0], doreg[1][0]); else q1_mfma_v(dp[1], av[ks % 3], doreg[1][ks]);
+      }
+      if constexpr (VHI > VLO) {
+        constexpr int lo = VLO + m * (VHI - VLO) / NSLOT, hi = VLO + (m + 1) * (VHI - VLO) / NSLOT;
+        q1_for<lo, hi>([&](auto k_c) __attribute__((always_inline)) { vstep(k_c, h); });
+        pin(h);  // without a use here the compiler sinks the softmax to its consumers
+      }
+      // the A operands of this slot's and the two previous slots' MFMAs stay in their registers through
+      // this slot (nothing the compiler places here may overwrite an operand an MFMA is still reading)
+      q1_for<(m >= 2 ? m - 2 : 0), m + 1>([&](auto p_c) __attribute__((always_inline)) {
+        constexpr int pm = decltype(p_c)::value, pks = pm / 4, psub = pm % 4;
+        if constexpr (psub < 2)
+          q1_keep(ak[pks % 3]);
+        else
+          q1_keep(av[pks % 3]);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    q1_fence4(s[0], s[1], dp[0], dp[1]);
+    asm volatile("" ::"v"(ak[0]), "v"(ak[1]), "v"(ak[2]), "v"(av[0]), "v"(av[1]), "v"(av[2]));
+  };
+  // softmax steps [VLO, VHI) of half-tile h alone
+  auto valu = [&](auto vlo_c, auto vhi_c, const Half& h) __attribute__((always_inline)) {
+    constexpr int VLO = decltype(vlo_c)::value, VHI = decltype(vhi_c)::value;
+    q1_for<VLO, VHI>([&](auto k_c) __attribute__((always_inline)) { vstep(k_c, h); });
+  };
+  // dQ^T += K^T dS^T for half kb of the tile in stage `sb` (dS packed in pk); optionally the next S/dP
+  // phase's first operand reads
+  auto dqp = [&](const char* sb, auto kb_c, bf16x8 (&pk)[2][2], const char* nsb, int nkb, auto first_c)
+                 __attribute__((always_inline)) {
+    constexpr int kb = decltype(kb_c)::value;
+    constexpr bool first = decltype(first_c)::value;  // the accumulators' first products
+    constexpr int NF = 2 * (D / 32);  // K^T fragments: (kk, db)
+    q1_fence_pk(pk);
+    bf16x8 ta[4];
+    auto tr = [&](int f, int x) __attribute__((always_inline)) {
+      ta[x] = lds_tr_a<D>(sb + C::K_OFF, (f % (D / 32)) * 32, kb * 32 + (f / (D / 32)) * 16, l);
+    };
+    tr(0, 0);
+    tr(1, 1);
+    if (nsb != nullptr) {  // the next S/dP phase's first operands
+      rd(nsb, nkb, 0, 0);
+      rd(nsb, nkb, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NSLOT = NF;
+    q1_for<0, NSLOT>([&](auto m_c) __attribute__((always_inline)) {
+      constexpr int f = decltype(m_c)::value, kk = f / (D / 32), db = f % (D / 32);
+      if constexpr (f + 2 < NF) tr(f + 2, (f + 2) % 4);
+      if constexpr (first && kk == 0) {
+        q1_mfma_a0(acc[0][db], ta[f % 4], pk[0][kk]);
+        q1_mfma_a0(acc[1][db], ta[f % 4], pk[1][kk]);
+      } else {
+        q1_mfma_a(acc[0][db], ta[f % 4], pk[0][kk]);
+        q1_mfma_a(acc[1][db], ta[f % 4], pk[1][kk]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // the last MFMAs' sources stay in their registers until these MFMAs have read them
+    asm volatile("s_nop 7\n\ts_nop 7" ::"v"(pk[0][0]), "v"(pk[0][1]), "v"(pk[1][0]), "v"(pk[1][1]), "v"(ta[0]),
+                 "v"(ta[1]), "v"(ta[2]), "v"(ta[3]));
+  };
+  auto need_mask = [&](int t) __attribute__((always_inline)) {
+    const int t0 = t * C::BN;
+    return t0 + C::BN - 1 > r_first || t0 < ds_last;
+  };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  using V0 = std::integral_constant<int, 0>;
+  using VN = std::integral_constant<int, NVSTEP>;
+  using FIRST = std::integral_constant<bool, true>;
+  using NOTFIRST = std::integral_constant<bool, false>;
+
+  dma(t_lo, 0);
+  if (t_lo + 1 <= t_hi) {
+    dma(t_lo + 1, 1);
+    dma_wait_prev();
+  } else {
+    dma_wait();
+  }
+  __syncthreads();
+  // phases: S(t,0) | dQ(t-1,1) | S(t,1) | dQ(t,0) | S(t+1,0) | ...; the softmax of a half-tile runs in
+  // the next S/dP phase
+  const Half hA0{sA, dpA, pkA, t_lo, 0, false};
+  {
+    const char* cur = smem;
+    const bool ahead = t_lo + 2 <= t_hi;
+    if (ahead) dma(t_lo + 2, 2);  // two tiles ahead: tile t_lo + 1 is in flight already
+    const Half hA{sA, dpA, pkA, t_lo, 0, need_mask(t_lo)};
+    sdp(cur, K0(), sA, dpA, V0(), V0(), hA0, false);
+    sdp(cur, K1(), sB, dpB, V0(), VN(), hA, false);  // (t_lo, 1st half)'s softmax
+    dqp(cur, K0(), pkA, nullptr, 0, FIRST());
+    q1_fence_acc(acc);  // the accumulators may be copied between register sets at the loop entry
+    if (ahead) dma_wait_prev(); else dma_wait();  // tile t_lo + 1 has landed
+    __syncthreads();
+  }
+  for (int t = t_lo + 1; t <= t_hi; ++t) {
+    const int u = t - t_lo;
+    const char* cur = smem + (u % 4) * C::STAGE;
+    const char* prv = smem + ((u + 3) % 4) * C::STAGE;
+    const bool ahead = t + 2 <= t_hi;
+    if (ahead) dma(t + 2, (u + 2) % 4);  // into tile t - 2's stage, last read before the previous barrier
+    const Half hBp{sB, dpB, pkB, t - 1, 1, need_mask(t - 1)};
+    const Half hA{sA, dpA, pkA, t, 0, need_mask(t)};
+    sdp(cur, K0(), sA, dpA, V0(), VN(), hBp, false);  // (t-1, 2nd half)'s softmax
+    dqp(prv, K1(), pkB, cur, 1, NOTFIRST());
+    sdp(cur, K1(), sB, dpB, V0(), VN(), hA, true);    // (t, 1st half)'s softmax
+    dqp(cur, K0(), pkA, nullptr, 0, NOTFIRST());
+    q1_fence_acc(acc);
+    if (ahead) dma_wait_prev(); else dma_wait();  // tile t + 1 has landed
+    __syncthreads();
+  }
+  // the last tile's second half
+  {
+    const Half hB{sB, dpB, pkB, t_hi, 1, need_mask(t_hi)};
+    valu(V0(), VN(), hB);
+    dqp(smem + ((t_hi - t_lo) % 4) * C::STAGE, K1(), pkB, nullptr, 0, NOTFIRST());
+  }
+  q1_fence_acc(acc);
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (!cvalid[j]) continue;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = acc[j][db][jj * 4 + e] * scale;
+        *reinterpret_cast<f32x4*>(dq + qoff[j] + db * 32 + jj * 8 + g * 4) = a;
+      }
+  }
+}
+
 int ilog2_pow2(int x) {
   int l = 0;
   while ((1 << l) < x) ++l;
@@ -652,7 +1047,7 @@ hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, con
   constexpr int NW = 8;
   static_assert(DkvCfg<128>::BNK == kKeyBlock && DkvCfg<128>::BQ == kColTile, "unit sizes of the order");
   static_assert(DkvCfg<64>::BNK == kKeyBlock && DkvCfg<64>::BQ == kColTile, "unit sizes of the order");
-  static_assert(DqCfg<128, NW>::BMC == kColBlock && DqCfg<128, NW>::BN == kKeyTile, "unit sizes of the order");
+  static_assert(Dq1wCfg<128>::BMC == kColBlock && Dq1wCfg<128>::BN == kKeyTile, "unit sizes of the order");
   static_assert(DqCfg<64, NW>::BMC == kColBlock && DqCfg<64, NW>::BN == kKeyTile, "unit sizes of the order");
   const int nkb = (int)key_blocks(N), ncb = (int)col_blocks(N, G);
   {
@@ -696,8 +1091,8 @@ hipError_t launch_attn_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, con
     const dim3 grid((unsigned)((int64_t)ncb * Hkv)), block(NW * 64);
     TimedLaunch timer("attn_bwd_dq", s);
     if (D == 128)
-      hipLaunchKernelGGL((dq_kernel<128, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, doc_start, order_col, dq,
-                         N, Hkv, lgG, sl2, scale);
+      hipLaunchKernelGGL((dq_kernel_1w<128>), grid, dim3(Dq1wCfg<128>::kThreads), 0, s, q, k, v, dout, lse, delta,
+                         doc_start, order_col, dq, N, Hkv, lgG, sl2, scale);
     else
       hipLaunchKernelGGL((dq_kernel<64, NW>), grid, block, 0, s, q, k, v, dout, lse, delta, doc_start, order_col, dq,
                          N, Hkv, lgG, sl2, scale);
