@@ -807,6 +807,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   };
 
+  // K^T fragments by transpose reads (as lds_tr_a): the lane's byte offsets within a tile for each 32-row
+  // block db of K^T and each of its two reads, so that the key-block and k-step parts of an address are
+  // immediate offsets (the row permutation and the chunk swizzle only touch the low four row bits)
+  int toff[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = l >> 4, s = l & 15;
+      const int n = db * 32 + (m & 1) * 16 + 4 * (s & 3);
+      const int x = (m >> 1) * 8 + (s >> 2) + h * 4;
+      toff[db][h] = lds_off<D>(tile_row(x), n >> 3) + (n & 7) * 2;
+    }
+  auto lds_tr_k = [&](const char* tile, int db, int k0) __attribute__((always_inline)) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + k0 * (D * 2) + toff[db][0]));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + k0 * (D * 2) + toff[db][1]));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, r);
+  };
+
   // half-tile buffers: A for first halves (keys 0-31 of a tile), B for second halves
   f32x16 sA[2], dpA[2], sB[2], dpB[2];
   bf16x8 pkA[2][2], pkB[2][2];
@@ -858,9 +880,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // operand ring of the S/dP phases: K and V fragments two ks steps ahead; a phase's first two are
   // read during the phase before it where that phase allows
   bf16x8 ak[3], av[3];
+  // the lane's byte offset of its K / V row chunk for each ks within a 32-key block (the block's rows are
+  // an immediate offset)
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lds_off<D>(lc, ks * 2 + g);
   auto rd = [&](const char* sb, int kb, int ks, int x) __attribute__((always_inline)) {
-    ak[x] = *reinterpret_cast<const bf16x8*>(sb + C::K_OFF + lds_off<D>(kb * 32 + lc, ks * 2 + g));
-    av[x] = *reinterpret_cast<const bf16x8*>(sb + C::V_OFF + lds_off<D>(kb * 32 + lc, ks * 2 + g));
+    ak[x] = *reinterpret_cast<const bf16x8*>(sb + C::K_OFF + kb * 32 * (D * 2) + koff[ks]);
+    av[x] = *reinterpret_cast<const bf16x8*>(sb + C::V_OFF + kb * 32 * (D * 2) + koff[ks]);
   };
   // S^T and dP^T of half kb of the tile in stage `sb` into (s, dp), with softmax steps [VLO, VHI) of
   // half-tile h between the MFMAs
@@ -925,7 +952,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     q1_fence_pk(pk);
     bf16x8 ta[4];
     auto tr = [&](int f, int x) __attribute__((always_inline)) {
-      ta[x] = lds_tr_a<D>(sb + C::K_OFF, (f % (D / 32)) * 32, kb * 32 + (f / (D / 32)) * 16, l);
+      ta[x] = lds_tr_k(sb + C::K_OFF, f % (D / 32), kb * 32 + (f / (D / 32)) * 16);
     };
     tr(0, 0);
     tr(1, 1);
