@@ -73,6 +73,13 @@ __device__ __forceinline__ int64_t col_offset(int64_t c, int lgG, int Hkv, int h
   return ((((c >> lgG) * Hkv + hk) << lgG) + (c & ((1 << lgG) - 1))) * D;
 }
 
+// a pointer that is the same in every lane, moved to scalar registers
+__device__ __forceinline__ const bf16* uniform_ptr(const bf16* p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x), hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return reinterpret_cast<const bf16*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
 // A operand of a 32x32x16 MFMA whose rows are the feature axis of a row-major
 // [64 rows][D] bf16 LDS tile (rows stored at tile_row(), chunks swizzled) and
 // whose k axis is the tile's row axis: lane l gets feature d0 + (l & 31) of
@@ -178,7 +185,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     int win) {
   using C = DkvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  UL_CODE_PAD(5);  // tile loop at 40 bytes into a 64-byte line (D = 128)
+  UL_CODE_PAD(2);  // tile loop at 40 bytes into a 64-byte line (D = 128)
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lc = l & 31;
   const int kbw = w & 3;   // this wave's 32-key block
   const int qh = w >> 2;   // this wave's half of every query tile
@@ -246,13 +253,30 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
     dch[i] = slot ^ ((((prow & 3) << 2) ^ ((prow >> 2) & 3)) & (CPR - 1));
     dr[i] = tile_row(prow);  // tile_row is an involution
   }
-  const int64_t tile_step = (int64_t)C::BQ * Hkv * D;
-  int64_t doff[C::RPT];
+  // A tile wholly inside the sequence starts at token tq * BQ / G; relative to that token every lane's
+  // source lies at the same byte offset in every tile, so those copies take a scalar base per tile and
+  // a 32-bit lane offset computed once (tile columns are whole tokens: G divides BQ)
+  uint32_t dlane[C::RPT];
 #pragma unroll
-  for (int i = 0; i < C::RPT; ++i)
-    doff[i] = col_offset((int64_t)tq_hi * C::BQ + dr[i], lgG, Hkv, hk, D) + dch[i] * 8;
+  for (int i = 0; i < C::RPT; ++i) dlane[i] = (uint32_t)((col_offset(dr[i], lgG, Hkv, hk, D) + dch[i] * 8) * 2);
+  const int64_t token_elems = (int64_t)(Hkv << lgG) * D;  // elements per token of q / dout
   typedef __attribute__((address_space(3))) char lds_char;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  const uint32_t lds_w = __builtin_amdgcn_readfirstlane(lds0 + w * C::RPT * 1024);
+  auto dma_full = [&](int st, int tq) {
+    const int64_t tok = ((int64_t)tq * C::BQ) >> lgG;
+    const bf16* qb = uniform_ptr(q + tok * token_elems);
+    const bf16* ob = uniform_ptr(dout + tok * token_elems);
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) {
+      const uint32_t mq = lds_w + st * C::STAGE + C::Q_OFF + i * 1024;
+      const uint32_t md = mq + (C::DO_OFF - C::Q_OFF);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(mq), "v"(dlane[i]),
+                   "s"(qb) : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(md), "v"(dlane[i]),
+                   "s"(ob) : "memory", "m0");
+    }
+  };
   auto dma = [&](int st, const int64_t* off) {
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) {
@@ -287,10 +311,8 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
       a_dl = delta[(int64_t)hk * NG + c];
     }
   };
-  auto gload_next = [&](int st) {  // the tile below the one loaded last (always inside the sequence)
-#pragma unroll
-    for (int i = 0; i < C::RPT; ++i) doff[i] -= tile_step;
-    dma(st, doff);
+  auto gload_next = [&](int st, int tq) {  // the tile below the one loaded last (always inside the sequence)
+    dma_full(st, tq);
     arow -= C::BQ >> lgG;
     acol -= C::BQ;
     if (tid < C::BQ) {
@@ -320,7 +342,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::kThreads) __attribute__((amdgpu_wav
   // constant (operand addresses then differ by immediate offsets only)
   auto tile = [&](auto stage, int tq) {
     constexpr int st = decltype(stage)::value;
-    if (tq > tq_lo) gload_next(st ^ 1);  // the other stage is free since the last barrier
+    if (tq > tq_lo) gload_next(st ^ 1, tq - 1);  // the other stage is free since the last barrier
     const char* b = smem + st * C::STAGE;
     const float* aux_lse = reinterpret_cast<const float*>(b + C::AUX_OFF);
     const float* aux_dl = aux_lse + C::BQ;
@@ -668,11 +690,6 @@ struct Dq1wCfg {
   static_assert(RPT * kThreads * 8 == BN * D, "tile copies must split evenly");
 };
 
-__device__ __forceinline__ const bf16* uniform_ptr(const bf16* p) {
-  const uint64_t x = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x), hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-  return reinterpret_cast<const bf16*>((uintptr_t)(((uint64_t)hi << 32) | lo));
-}
 __device__ __forceinline__ void q1_mfma_v0(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
 }
