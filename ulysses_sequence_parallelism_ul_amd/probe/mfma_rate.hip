@@ -226,9 +226,11 @@ mix_kernel(const u32x4* __restrict__ in, float* __restrict__ out, int iters) {
 // tiles (D = 128, two tiles of the forward, one of dK/dV, half a tile of dQ):
 //   0 forward: 64 MFMAs, 64 b128 reads, 64 exponentials, 265 other VALU, 8 staged 16-byte loads;
 //   1 dQ:      48 MFMAs, 16 b128 + 16 transpose reads, 32 exponentials, 136 other VALU, 4 loads;
-//   2 dK/dV:   64 MFMAs, 80 b128 + 64 transpose reads, 32 exponentials, 149 other VALU, 8 loads.
+//   2 dK/dV:   64 MFMAs, 80 b128 + 64 transpose reads, 32 exponentials, 124 other VALU, 8 loads.
 // The compiled probe bodies hold the same counts: their VALU argument is below the target by the
-// address arithmetic the compiler adds to each body (25, 14 and 26 instructions).  The dQ kernel
+// address arithmetic the compiler adds to each body (25, 14 and 26 instructions), except that the
+// dK/dV body holds 138 other VALU instructions, not 124: every loaded word needs a consumer here
+// (NV >= NB + NE), which puts the floor of that body at 112 + 26.  The dQ kernel
 // runs one wave per SIMD (each fragment it reads feeds two MFMAs); the probe keeps two, so its
 // rate is that of the mix with the latencies hidden.
 constexpr int kMixMfmas[3] = {64, 48, 64};
@@ -312,7 +314,7 @@ int ul_probe_mix_rate(int kind, int launches, int iters, const void* operands, s
     else if (kind == 1)
       hipLaunchKernelGGL((mix_kernel<48, 16, 16, 32, 122, 4>), dim3(kMixBlocks), dim3(kMixThreads), 0, s, in, o, iters);
     else
-      hipLaunchKernelGGL((mix_kernel<64, 80, 64, 32, 123, 8>), dim3(kMixBlocks), dim3(kMixThreads), 0, s, in, o, iters);
+      hipLaunchKernelGGL((mix_kernel<64, 80, 64, 32, 112, 8>), dim3(kMixBlocks), dim3(kMixThreads), 0, s, in, o, iters);
   };
   hipEvent_t a = nullptr, b = nullptr;
   if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return 2;
