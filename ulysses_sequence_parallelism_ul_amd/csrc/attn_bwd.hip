@@ -132,10 +132,11 @@ __global__ void __launch_bounds__(256) delta_bf16_kernel(const bf16* __restrict_
 // through LDS at the end.
 // Prologue padding (executed once per wave) that places a kernel's tile loop
 // at a measured-good offset within the 64-byte lines the instructions are
-// fetched in: with its loop starting 44 bytes into a line dQ ran 3 % slower
-// than at 0, 24 or 32 bytes (same box, N = 1M, identical loop code).  The
-// counts hold for the code as it stands; any change to a prologue moves its
-// loop (tests/test_code_layout.py disassembles the build and checks both).
+// fetched in: an earlier eight-wave dQ kernel ran 3 % slower with its loop 44
+// bytes into a line than at 0, 24 or 32 (same box, N = 1M, identical loop
+// code), and dK/dV's offsets spread over 1.5 %.  The count holds for the code
+// as it stands; any change to a prologue moves its loop
+// (tests/test_code_layout.py disassembles the build and checks the offsets).
 #define UL_CODE_PAD(n) asm volatile(".rept " #n "\ns_nop 0\n.endr")
 
 template <int D>
