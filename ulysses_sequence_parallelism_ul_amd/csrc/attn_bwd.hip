@@ -697,6 +697,10 @@ __device__ __forceinline__ void q1_mfma_v0(f32x16& d, const bf16x8& a, const bf1
 __device__ __forceinline__ void q1_mfma_v(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
+// the first MFMA of a chain seeded with a register block the chain does not overwrite
+__device__ __forceinline__ void q1_mfma_vc(f32x16& d, const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+}
 __device__ __forceinline__ void q1_mfma_a0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(acc) : "v"(a), "v"(b));
 }
@@ -786,6 +790,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   }
   f32x16 acc[2][D / 32];  // set by the first tile's first dQ MFMAs (no zero fill to copy between registers)
+  // -Delta of the lane's column in the first 32-column half: the seed of that half's dP^T chains, so they
+  // produce dP - Delta directly (every lane's 16 values of a dP^T block belong to its one column); the
+  // second half keeps the subtraction, since a second 16-register block does not fit beside the rest
+  f32x16 ndl0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndl0[i] = -dl[0];
 
   // DMA of a K / V tile: lane l of wave w's i-th copy fills byte (w * RPT + i) * 1024 + 16 l of the tile,
   // the row and chunk the permuted, swizzled layout keeps there; keys past the end read the last key
@@ -883,7 +893,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = (st - 9) * 4 + e;
-        sj[i] *= h.dp[j][i] - dl[j];
+        if constexpr (j == 0)
+          sj[i] *= h.dp[j][i];  // the chain started from -Delta
+        else
+          sj[i] *= h.dp[j][i] - dl[j];
       }
     } else {
       h.pk[j][st - 13] = pack8(sj, (st - 13) * 8);
@@ -932,7 +945,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       } else if constexpr (sub == 1) {
         if constexpr (ks == 0) q1_mfma_v0(s[1], ak[0], qreg[1][0]); else q1_mfma_v(s[1], ak[ks % 3], qreg[1][ks]);
       } else if constexpr (sub == 2) {
-        if constexpr (ks == 0) q1_mfma_v0(dp[0], av[0], doreg[0][0]); else q1_mfma_v(dp[0], av[ks % 3], doreg[0][ks]);
+        if constexpr (ks == 0) q1_mfma_vc(dp[0], av[0], doreg[0][0], ndl0); else q1_mfma_v(dp[0], av[ks % 3], doreg[0][ks]);
       } else {
         if constexpr (ks == 0) q1_mfma_v0(dp[1], av[0], doreg[1][0]); else q1_mfma_v(dp[1], av[ks % 3], doreg[1][ks]);
       }
