@@ -790,12 +790,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   }
   f32x16 acc[2][D / 32];  // set by the first tile's first dQ MFMAs (no zero fill to copy between registers)
-  // -Delta of the lane's column in the first 32-column half: the seed of that half's dP^T chains, so they
+  // -Delta of the lane's column in each 32-column half: the seeds of that half's dP^T chains, so they
   // produce dP - Delta directly (every lane's 16 values of a dP^T block belong to its one column); the
-  // second half keeps the subtraction, since a second 16-register block does not fit beside the rest
+  // two blocks push the column offsets out to scratch across the loop (reloaded for the final stores)
   f32x16 ndl0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ndl0[i] = -dl[0];
+  f32x16 ndl1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndl1[i] = -dl[1];
 
   // DMA of a K / V tile: lane l of wave w's i-th copy fills byte (w * RPT + i) * 1024 + 16 l of the tile,
   // the row and chunk the permuted, swizzled layout keeps there; keys past the end read the last key
@@ -893,10 +896,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = (st - 9) * 4 + e;
-        if constexpr (j == 0)
-          sj[i] *= h.dp[j][i];  // the chain started from -Delta
-        else
-          sj[i] *= h.dp[j][i] - dl[j];
+        sj[i] *= h.dp[j][i];  // the chain started from -Delta
       }
     } else {
       h.pk[j][st - 13] = pack8(sj, (st - 13) * 8);
@@ -947,7 +947,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       } else if constexpr (sub == 2) {
         if constexpr (ks == 0) q1_mfma_vc(dp[0], av[0], doreg[0][0], ndl0); else q1_mfma_v(dp[0], av[ks % 3], doreg[0][ks]);
       } else {
-        if constexpr (ks == 0) q1_mfma_v0(dp[1], av[0], doreg[1][0]); else q1_mfma_v(dp[1], av[ks % 3], doreg[1][ks]);
+        if constexpr (ks == 0) q1_mfma_vc(dp[1], av[0], doreg[1][0], ndl1); else q1_mfma_v(dp[1], av[ks % 3], doreg[1][ks]);
       }
       if constexpr (VHI > VLO) {
         constexpr int lo = VLO + m * (VHI - VLO) / NSLOT, hi = VLO + (m + 1) * (VHI - VLO) / NSLOT;
