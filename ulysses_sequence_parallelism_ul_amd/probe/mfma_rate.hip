@@ -225,7 +225,7 @@ mix_kernel(const u32x4* __restrict__ in, float* __restrict__ out, int iters) {
 // The mixes, counted in the compiled tile loops of the attention kernels on fully visible
 // tiles (D = 128, two tiles of the forward, one of dK/dV, half a tile of dQ):
 //   0 forward: 64 MFMAs, 64 b128 reads, 64 exponentials, 265 other VALU, 8 staged 16-byte loads;
-//   1 dQ:      48 MFMAs, 16 b128 + 16 transpose reads, 32 exponentials, 136 other VALU, 4 loads;
+//   1 dQ:      48 MFMAs, 16 b128 + 16 transpose reads, 32 exponentials, 107 other VALU, 4 loads;
 //   2 dK/dV:   64 MFMAs, 80 b128 + 64 transpose reads, 32 exponentials, 124 other VALU, 8 loads.
 // The compiled probe bodies hold the same counts: their VALU argument is below the target by the
 // address arithmetic the compiler adds to each body (25, 14 and 26 instructions), except that the
@@ -312,7 +312,7 @@ int ul_probe_mix_rate(int kind, int launches, int iters, const void* operands, s
     if (kind == 0)
       hipLaunchKernelGGL((mix_kernel<64, 64, 0, 64, 240, 8>), dim3(kMixBlocks), dim3(kMixThreads), 0, s, in, o, iters);
     else if (kind == 1)
-      hipLaunchKernelGGL((mix_kernel<48, 16, 16, 32, 122, 4>), dim3(kMixBlocks), dim3(kMixThreads), 0, s, in, o, iters);
+      hipLaunchKernelGGL((mix_kernel<48, 16, 16, 32, 93, 4>), dim3(kMixBlocks), dim3(kMixThreads), 0, s, in, o, iters);
     else
       hipLaunchKernelGGL((mix_kernel<64, 80, 64, 32, 112, 8>), dim3(kMixBlocks), dim3(kMixThreads), 0, s, in, o, iters);
   };
