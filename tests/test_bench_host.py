@@ -146,6 +146,31 @@ def test_power_sampler_without_a_device_reports_nothing():
     assert out["samples"] == 0 and out["board_power_w"] is None and out["gfx_clock_mhz"] is None
 
 
+def test_power_sampler_starts_no_process_under_rocprofv3(monkeypatch):
+    """Inside a rocprofv3 run (ROCPROF_* in the environment) the sampler starts no amd-smi process at all,
+    even with a device present: the profiler's preload would make amd-smi's `env` exec from a process that
+    has initialised the GPU."""
+    class _Props:
+        pci_domain_id, pci_bus_id, pci_device_id = 0, 0x75, 0
+
+    class _Cuda:
+        class cuda:
+            @staticmethod
+            def get_device_properties(i):
+                return _Props
+
+    started = []
+    monkeypatch.setattr(bench.subprocess, "run", lambda *a, **k: started.append(a) or (_ for _ in ()).throw(
+        AssertionError("a process was started")))
+    monkeypatch.setenv("ROCPROF_OUTPUT_PATH", "/tmp/x")
+    assert bench.under_profiler()
+    s = bench.PowerSampler(_Cuda)
+    with s:
+        pass
+    assert started == [] and s.summary()["samples"] == 0
+    assert not bench.under_profiler({"PATH": "/usr/bin", "HIP_VISIBLE_DEVICES": "0"})
+
+
 def test_power_clock_context_scales_the_peak_by_the_clock():
     roof = {"bound": "mfma", "achieved": 1100.0}
     out = bench.power_clock_context({"samples": 3, "gfx_clock_mhz": 1800.0, "board_power_w": 1330.0}, roof)
