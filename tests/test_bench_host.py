@@ -177,7 +177,10 @@ def test_power_clock_context_scales_the_peak_by_the_clock():
     assert out["mfma_peak_at_clock_tflops"] == pytest.approx(1875.0)
     assert out["dominant_frac_at_clock"] == pytest.approx(1100.0 / 1875.0)
     out = bench.power_clock_context({"samples": 0, "gfx_clock_mhz": None, "board_power_w": None}, roof)
-    assert "mfma_peak_at_clock_tflops" not in out
+    assert out["mfma_peak_at_clock_tflops"] is None and out["dominant_frac_at_clock"] is None
+    # one or two polls of a short timed region may see the board idle (163 MHz once gave a "fraction" of 6.5)
+    out = bench.power_clock_context({"samples": 1, "gfx_clock_mhz": 163.0, "board_power_w": 255.0}, roof)
+    assert out["mfma_peak_at_clock_tflops"] is None and out["dominant_frac_at_clock"] is None and out["note"]
 
 
 def test_cpu_host_info_and_extrapolation():
